@@ -1,0 +1,331 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--ctx 32768] [--no-cpu]
+
+A step is one pass of the whole decode hot path for one layer of a B=1 batch
+(32 q / 8 KV heads, head_dim 128, bf16, 40K-slot pool of shuffled 16-token
+pages): the index step (kv_indptr, new-token location, split plan), the store
+of the new token's K/V, the split-KV partial kernel and the log-sum-exp merge.
+Layers rotate over an 8-layer pool (1.34 GB of K+V) so that successive steps
+read K/V from HBM, not from the 256 MB Infinity Cache.
+
+The headline line is the 32K context; the other contexts (1K, 4K, 16K) are
+reported under "detail". The timed region is K steps enqueued behind a short
+device-side spin, so the GPU runs them back to back without host launch gaps;
+ms_per_step comes from HIP events on the launch stream around the K steps, and
+the partial kernel's duration from events around each of its launches.
+The CPU oracle (fp64 NumPy) is timed on a bounded sample for cpu_baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--ctx", type=int, nargs="*", default=[1024, 4096, 16384, 32768])
+    p.add_argument("--headline", type=int, default=32768)
+    p.add_argument("--split-tokens", type=int, default=256)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--graph", action="store_true", help="also time HIP-graph replay")
+    return p.parse_args()
+
+
+_SPIN_RATE = None
+
+
+def spin_cycles_per_s() -> float:
+    """Rate of the counter torch.cuda._sleep spins on, measured once with events."""
+    global _SPIN_RATE
+    if _SPIN_RATE is None:
+        import torch
+
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(100000)
+        a.record()
+        torch.cuda._sleep(2000000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_RATE = 2000000 / (a.elapsed_time(b) * 1e-3)
+    return _SPIN_RATE
+
+
+class DecodeBench:
+    """Device state of one B=1 decode workload and its prepared library calls."""
+
+    def __init__(self, ctx: int, n_layers: int, split_tokens: int, seed: int):
+        import torch
+
+        from paged_kv_cache_184_amd import ops
+        from paged_kv_cache_184_amd import workloads as W
+
+        self.torch, self.ops = torch, ops
+        b = W.b1_decode(ctx, n_layers=n_layers)
+        self.b = b
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shape = (b.n_layers, b.n_slots, b.n_kv_heads, b.head_dim)
+        self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        live = torch.from_numpy(b.live_slots).to(dev).long()
+        kv = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
+        kv = kv.to(torch.bfloat16)
+        for layer in range(b.n_layers):  # identical layers
+            self.k_pool[layer, live] = kv[0]
+            self.v_pool[layer, live] = kv[1]
+        del kv
+        B = b.batch
+        self.q = torch.randn((B, b.n_q_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.k_new = torch.randn((B, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.v_new = torch.randn((B, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.r2t = torch.from_numpy(b.req_to_token).to(dev)
+        self.rows = torch.from_numpy(b.req_pool_indices).to(dev)
+        self.lens = torch.from_numpy(b.seq_lens).to(dev)
+        self.meta = ops.make_meta(self.r2t, self.rows, self.lens)
+        max_splits = max(1, -(-ctx // split_tokens))
+        self.split = ops.split_cfg(max_splits, 0, split_tokens)
+        self.ws = ops.alloc_decode_workspace(B, b.n_q_heads, b.head_dim, max_splits)
+        self.out = torch.empty_like(self.q)
+        self.kv_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.loc = torch.empty(B, dtype=torch.int32, device=dev)
+        self.splits = torch.empty(B, dtype=torch.int32, device=dev)
+        self.calls = []
+        for layer in range(b.n_layers):
+            self.calls.append((
+                ops.prepare_metadata(self.meta, ops.PKV_MODE_DECODE, self.split, self.kv_indptr,
+                                     self.loc, self.splits),
+                ops.prepare_kv_store(self.k_pool, self.v_pool, layer, self.k_new, self.v_new,
+                                     self.loc),
+                ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale,
+                                   self.split, self.ws, self.out, stage="partials"),
+                ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale,
+                                   self.split, self.ws, self.out, stage="merge"),
+            ))
+
+    # algorithmic bytes
+    def kv_bytes(self) -> int:
+        return self.b.kv_bytes_logical()
+
+    def partial_kernel_bytes(self) -> int:
+        b = self.b
+        L = int(b.seq_lens.sum())
+        return self.kv_bytes() + b.batch * b.n_q_heads * b.head_dim * 2 + L * 4
+
+    def step_bytes(self) -> int:
+        b = self.b
+        return self.partial_kernel_bytes() + b.batch * b.n_q_heads * b.head_dim * 2
+
+    def step(self, i: int, ev=None):
+        meta_call, store_call, part_call, merge_call = self.calls[i % len(self.calls)]
+        meta_call()
+        store_call()
+        if ev is not None:
+            ev[0].record()
+        part_call()
+        if ev is not None:
+            ev[1].record()
+        merge_call()
+
+    def run(self, steps: int, warmup: int):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        # host time to enqueue one step, and the device spin rate, so the hold
+        # below lasts longer than enqueueing all K steps
+        t = time.perf_counter()
+        for i in range(8):
+            self.step(i)
+        enqueue_s = (time.perf_counter() - t) / 8
+        torch.cuda.synchronize()
+        cycles = int(min(2e9, max(1e5, 2.0 * steps * enqueue_s * spin_cycles_per_s())))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        # hold the stream so the host enqueues the K steps ahead of the GPU; the
+        # start event is recorded after the hold
+        torch.cuda._sleep(cycles)
+        start.record()
+        for i in range(steps):
+            self.step(i, evs[i])
+        end.record()
+        torch.cuda.synchronize()
+        host_s = time.perf_counter() - t0
+        step_ms = start.elapsed_time(end) / steps
+        part_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return step_ms, part_ms, host_s
+
+    def run_graph(self, steps: int):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(len(self.calls)):
+                self.step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        n_per_graph = len(self.calls)
+        with torch.cuda.graph(g):
+            for i in range(n_per_graph):
+                self.step(i)
+        torch.cuda.synchronize()
+        reps = max(1, steps // n_per_graph)
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * n_per_graph)
+
+    def check(self) -> float:
+        """Max abs error of the last output against the oracle (layer 0 state)."""
+        import oracle as O
+
+        b = self.b
+        layer = 0
+        self.step(0)
+        self.torch.cuda.synchronize()
+        L = int(b.seq_lens[0])
+        slots = b.req_to_token[b.req_pool_indices[0], :L]
+        idx = self.torch.from_numpy(slots.astype(np.int64)).to("cuda")
+        k = self.k_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
+        v = self.v_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
+        r2t = np.arange(L, dtype=np.int32)[None]
+        ref = O.decode_attention(self.q.float().cpu().numpy(), k, v, 0, r2t,
+                                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
+        return float(np.abs(self.out.float().cpu().numpy() - ref).max())
+
+    def oracle_inputs(self):
+        b = self.b
+        L = int(b.seq_lens[0])
+        slots = b.req_to_token[b.req_pool_indices[0], :L]
+        idx = self.torch.from_numpy(slots.astype(np.int64)).to("cuda")
+        k = self.k_pool[0].index_select(0, idx).float().cpu().numpy()[None]
+        v = self.v_pool[0].index_select(0, idx).float().cpu().numpy()[None]
+        return (self.q.float().cpu().numpy(), k, v, np.arange(L, dtype=np.int32)[None],
+                np.array([0], np.int32), np.array([L], np.int32), b.scale)
+
+
+def cpu_baseline(db: DecodeBench, seconds: float):
+    """Time the fp64 oracle on the headline workload until ``seconds`` of CPU
+    work have run; report KV GB/s in the same unit as the GPU."""
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    args = db.oracle_inputs()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.decode_attention(*args[:4], args[4], args[5], args[6])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = db.kv_bytes() * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full oracle decode calls (B=1, ctx {db.b.seq_lens[0]}, 32 q heads) "
+                      f"in {el:.1f} s; BLAS threads as reported by threadpoolctl"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    detail = {}
+    head = None
+    for ctx in args.ctx:
+        db = DecodeBench(ctx, n_layers=8, split_tokens=args.split_tokens, seed=184_002 + ctx)
+        step_ms, part_ms, host_s = db.run(args.steps, args.warmup)
+        err = db.check()
+        entry = {
+            "us_per_step": round(step_ms * 1e3, 2),
+            "kv_gbs": round(db.kv_bytes() / (step_ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * db.step_bytes() / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "partial_kernel_us": round(part_ms * 1e3, 2),
+            "partial_kernel_gbs": round(db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9, 1),
+            "splits": int(db.split.max_splits),
+            "max_abs_err": err,
+        }
+        if args.graph:
+            g_ms = db.run_graph(args.steps)
+            entry["graph_us_per_step"] = round(g_ms * 1e3, 2)
+            entry["graph_kv_gbs"] = round(db.kv_bytes() / (g_ms * 1e-3) / 1e9, 1)
+        detail[f"{ctx // 1024}k"] = entry
+        print(f"# ctx {ctx}: {entry}", file=sys.stderr, flush=True)
+        if ctx == args.headline:
+            head = (db, step_ms, part_ms, host_s)
+        else:
+            del db
+            torch.cuda.empty_cache()
+    if head is None:
+        raise SystemExit("--headline must be one of --ctx")
+    db, step_ms, part_ms, host_s = head
+    kv_gbs = db.kv_bytes() / (step_ms * 1e-3) / 1e9
+    achieved = db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9
+    line = {
+        "metric": "paged decode attn KV GB/s (% HBM peak) + us/step, B=1..64, 1K-32K ctx",
+        "value": round(kv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"b1_decode_{args.headline // 1024}k", "batch": 1,
+                   "context": args.headline, "n_q_heads": 32, "n_kv_heads": 8, "head_dim": 128,
+                   "kv_dtype": "bf16", "pool_slots": 40960, "layers_rotated": 8,
+                   "slot_layout": "shuffled 16-token pages", "split_tokens": args.split_tokens},
+        "pct_hbm_peak": detail[f"{args.headline // 1024}k"]["pct_hbm_peak"],
+        "us_per_step": round(step_ms * 1e3, 2),
+        "host_s_timed_region": round(host_s, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_partial_kernel<bf16,128,4>"},
+        "detail": detail,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(db, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

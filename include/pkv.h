@@ -1,0 +1,237 @@
+/*
+ * pkv.h -- attention over a paged, slot-indexed KV cache on AMD MI355X (gfx950).
+ *
+ * A C ABI: plain device pointers, sizes and a HIP stream; no framework types.
+ * Every entry point validates its host-visible arguments first and, on any
+ * error, returns a status without enqueueing or writing anything. On success
+ * the work is enqueued on `stream` and the call returns without synchronising;
+ * the library never allocates device memory, never reads device data on the
+ * host (except pkv_validate_meta, a debug aid) and keeps no pointer after it
+ * returns, so the calls may be captured into a HIP graph.
+ *
+ * Citation key for the pages this library follows (AstrAI commit pages; a
+ * "bullet" is one line of the commit message shown on that page):
+ *   P1  commit 398e8a3e, page for tests/inference/test_cache.py
+ *   P2  commit 8e39d9d8, page for astrai/inference/workspace.py
+ *   P4  commit e58a728b, page for docs/developer/architecture.md
+ *
+ * Data model (P1, bullets on the 4D KVStorage layout and on single advanced
+ * indexing buffer[layer_id, loc]; P1, bullet on int32 page-table, request-row
+ * and cache-location indices):
+ *   K and V pools: two contiguous tensors [n_layers, n_slots, n_kv_heads, head_dim].
+ *   req_to_token:  int32 [n_req_rows, stride]; entry (r, j) is the slot holding
+ *                  position j of the request stored in row r.
+ *   seq_lens[b]:   keys visible to request b's last query, new tokens included.
+ *   qo_indptr:     int32 [batch + 1]; request b's new tokens are the packed rows
+ *                  qo_indptr[b] .. qo_indptr[b+1]-1 (P4, bullet on cumulative
+ *                  query lengths).
+ *   Query head h of a request reads KV head h / (n_q_heads / n_kv_heads).
+ *
+ * Supported: dtype F32 or BF16 (Q, K, V and output share it; accumulation is
+ * always fp32), head_dim 64 or 128, group size n_q_heads / n_kv_heads in
+ * {1, 2, 4, 8, 16}.
+ *
+ * Memory safety: kernels clamp every device-supplied index to the buffer it
+ * addresses (slots to [0, n_slots), request rows to [0, n_req_rows), positions
+ * to [0, stride), packed rows to [0, total_q)), so malformed metadata gives
+ * undefined values but never an out-of-bounds access. pkv_validate_meta
+ * reports such metadata.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* ---- status codes ---------------------------------------------------- */
+typedef int32_t pkv_status;
+#define PKV_OK 0
+#define PKV_EINVAL 1       /* null pointer, negative size, index out of range, bad mode */
+#define PKV_EDTYPE 2       /* dtype code not F32 / BF16 */
+#define PKV_ESHAPE 3       /* inconsistent shapes, e.g. n_q_heads % n_kv_heads != 0 */
+#define PKV_EALIGN 4       /* tensor pointer not 16-byte aligned, workspace not 256-byte aligned */
+#define PKV_EWORKSPACE 5   /* workspace smaller than pkv_decode_workspace_bytes() */
+#define PKV_EUNSUPPORTED 6 /* head_dim or group size outside the supported set */
+#define PKV_EHIP 7         /* a kernel launch failed; see pkv_last_error() */
+
+/* ---- dtypes and modes -------------------------------------------------- */
+#define PKV_F32 0
+#define PKV_BF16 1
+
+#define PKV_MODE_DECODE 0
+#define PKV_MODE_PREFILL 1
+
+/* Split boundaries are multiples of this many tokens. */
+#define PKV_SPLIT_ALIGN 16
+/* Largest accepted max_splits. */
+#define PKV_MAX_SPLITS 4096
+
+/* ---- descriptors ------------------------------------------------------- */
+
+/* The KV pools. k and v are device pointers, 16-byte aligned, to contiguous
+ * [n_layers, n_slots, n_kv_heads, head_dim] tensors of `dtype`. Owned by the caller. */
+typedef struct pkv_kv_pool {
+  void* k;
+  void* v;
+  int64_t n_layers;
+  int64_t n_slots;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t reserved;
+} pkv_kv_pool;
+
+/* Per-batch metadata; all arrays are int32 device pointers owned by the caller.
+ *   req_to_token      [n_req_rows, req_to_token_stride]
+ *   req_pool_indices  [batch]  row of req_to_token used by request b
+ *   seq_lens          [batch]  L_b (a decode row with L_b = 0 is padding)
+ *   qo_indptr         [batch+1] packed new-token offsets; required for prefill,
+ *                     ignored (may be NULL) for decode
+ *   kv_indptr         [batch+1] optional (may be NULL); exclusive prefix sum
+ *                     of seq_lens as written by pkv_build_metadata. The kernels
+ *                     address K/V through req_to_token and do not read it;
+ *                     pkv_validate_meta checks it when present. */
+typedef struct pkv_batch_meta {
+  const int32_t* req_to_token;
+  int64_t req_to_token_stride;
+  int32_t n_req_rows;
+  int32_t batch;
+  const int32_t* req_pool_indices;
+  const int32_t* seq_lens;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+} pkv_batch_meta;
+
+/* How decode splits each request's keys (P1, bullets on workspace-owned
+ * decode_o_part / decode_ml_part split partials).
+ *   max_splits    capacity of the workspace per (request, q head), 1..PKV_MAX_SPLITS
+ *   fixed_splits  > 0: request this many splits; 0: automatic
+ *   split_tokens  automatic mode requests ceil(L_b / split_tokens) splits;
+ *                 a multiple of PKV_SPLIT_ALIGN, >= PKV_SPLIT_ALIGN
+ * For a request of length L > 0 the requested count R is clamped to
+ * [1, max_splits]; the chunk is C = round_up(ceil(L / R), PKV_SPLIT_ALIGN);
+ * the split count is S = ceil(L / C) (never more than R, never an empty
+ * split) and split s covers positions [s*C, min(L, (s+1)*C)). S = 0 when L = 0. */
+typedef struct pkv_split_cfg {
+  int32_t max_splits;
+  int32_t fixed_splits;
+  int32_t split_tokens;
+  int32_t reserved;
+} pkv_split_cfg;
+
+/* ---- library info ------------------------------------------------------ */
+int pkv_abi_version(void);
+const char* pkv_status_str(pkv_status s);
+/* Message describing the last failure of a pkv_* call on the calling thread
+ * ("" if none). The pointer stays valid until the next pkv_* call on the thread. */
+const char* pkv_last_error(void);
+
+/* ---- a2: store new K/V at cache locations -------------------------------
+ * For every t < n_tokens with 0 <= loc[t] < n_slots:
+ *   k[layer, loc[t], :, :] = k_new[t];  v[layer, loc[t], :, :] = v_new[t]
+ * (P1, bullet on single advanced indexing buffer[layer_id, loc]). Negative
+ * locations (padded rows) and locations >= n_slots are skipped. The copy is
+ * bit-exact; locations must be unique within one call (duplicates race).
+ * k_new, v_new: device [n_tokens, n_kv_heads, head_dim] of the pool dtype,
+ * 16-byte aligned. loc: device int32 [n_tokens]. n_tokens == 0 is a no-op. */
+pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_new,
+                        const void* v_new, const int32_t* loc, int64_t n_tokens,
+                        hipStream_t stream);
+
+/* ---- a1: index step ----------------------------------------------------
+ * Writes, each only if its pointer is non-NULL (P1, bullet on updating
+ * position_ids / seq_lens / kv_indptr in place each decode step):
+ *   kv_indptr_out[0..batch]  exclusive prefix sum of seq_lens (int32; totals
+ *                            of 2^31 or more wrap and are undefined)
+ *   loc_out                  cache locations of the new tokens:
+ *     DECODE:  loc_out[b] = req_to_token[r_b, L_b - 1], or -1 when L_b == 0
+ *     PREFILL: loc_out[qo_indptr[b] + i] = req_to_token[r_b, L_b - n_b + i],
+ *              i < n_b = qo_indptr[b+1] - qo_indptr[b]; rows >= loc_capacity
+ *              are skipped
+ *   splits_out[b]            decode split count S_b under `split` (DECODE only;
+ *                            must be NULL in PREFILL mode)
+ * loc_capacity: length of loc_out in elements (>= batch for DECODE). */
+pkv_status pkv_build_metadata(const pkv_batch_meta* meta, int32_t mode, pkv_split_cfg split,
+                              int32_t* kv_indptr_out, int32_t* loc_out, int64_t loc_capacity,
+                              int32_t* splits_out, hipStream_t stream);
+
+/* ---- decode workspace ----------------------------------------------------
+ * Bytes of workspace one decode call over `batch` requests needs. Layout
+ * (fp32, offsets from the workspace start, which must be 256-byte aligned):
+ *   o_part  at 0:               [batch, n_q_heads, max_splits, head_dim]
+ *           o_part[b,h,s,:] is split s's output, normalised by its own l
+ *   ml_part at round_up(batch*n_q_heads*max_splits*head_dim*4, 256):
+ *           [batch, n_q_heads, max_splits, 2] = (m, l) with
+ *           l = sum_{j in split} exp(x_j - m), x_j = scale * q.k_j; m is a
+ *           finite stabiliser the kernel picks (one of the x_j seen so far), so
+ *           only m + ln(l), the split's log-sum-exp, is uniquely defined.
+ * Entries for s >= S_b are not written. Returns 0 if an argument is not positive
+ * or max_splits > PKV_MAX_SPLITS. A workspace sized for batch B serves any batch <= B. */
+size_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
+                                  int32_t max_splits);
+
+/* ---- a3 + a4: split-KV paged decode attention ----------------------------
+ * One query token per request: for request b and q head h (KV head h/g),
+ *   out[b, h, :] = softmax_j(scale * q[b,h,:] . K[j]) V[j],  j < L_b,
+ * with K[j], V[j] read at slot req_to_token[r_b, j] of `layer`. Computed as
+ * split partials in the workspace (a3) followed by a log-sum-exp merge (a4);
+ * rows with L_b = 0 produce zeros. q, out: device [batch, n_q_heads, head_dim]
+ * of the pool dtype, 16-byte aligned; out is rounded to nearest-even.
+ * The result is bit-identical run to run and does not depend on where the
+ * slots sit in the pool. */
+pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                 int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
+                                 pkv_split_cfg split, void* workspace, size_t ws_bytes,
+                                 void* out, hipStream_t stream);
+
+/* a3 alone: writes the split partials of pkv_paged_decode_attn into the workspace. */
+pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                               int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
+                               pkv_split_cfg split, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* a4 alone: merges the partials a pkv_decode_partials call with the same meta,
+ * n_q_heads, head_dim and split left in the workspace:
+ *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s exp(m_s - max_s' m_s'). */
+pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32_t head_dim,
+                            int32_t dtype, pkv_split_cfg split, const void* workspace,
+                            size_t ws_bytes, void* out, hipStream_t stream);
+
+/* ---- a5: ragged packed paged prefill --------------------------------------
+ * New token i < n_b of request b (packed row t = qo_indptr[b] + i) attends,
+ * per q head h with KV head h/g, to positions j <= L_b - n_b + i when causal
+ * (bottom-right aligned: the cached prefix plus the earlier new tokens), or to
+ * all j < L_b when not (P4, bullets on packing prompts with a shared prefix
+ * start into one forward; P1, bullet on cached prefix pages). The new tokens'
+ * K/V must already be stored (pkv_kv_store). q, out: device
+ * [total_q, n_q_heads, head_dim], 16-byte aligned. max_q_len >= every n_b sizes
+ * the grid (rows i >= max_q_len are not computed). QK^T and PV run on bf16 MFMA
+ * for BF16 (P is rounded to bf16 for PV; the row sums use those rounded values). */
+pkv_status pkv_paged_prefill_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                  int32_t n_q_heads, const pkv_batch_meta* meta,
+                                  int32_t total_q, int32_t max_q_len, float scale,
+                                  int32_t causal, void* out, hipStream_t stream);
+
+/* ---- debug validator --------------------------------------------------------
+ * Synchronous: copies the metadata to the host (on `stream`, then waits) and
+ * checks req_pool_indices in [0, n_req_rows), 0 <= seq_lens <= stride, slots
+ * of every live position in [0, n_slots), and for PREFILL qo_indptr
+ * non-decreasing from 0 with n_b <= L_b and qo_indptr[batch] <= total_q; when
+ * meta->kv_indptr is set, that it equals the prefix sum of seq_lens.
+ * Returns PKV_EINVAL with a message naming the first bad entry. Not for the hot path. */
+pkv_status pkv_validate_meta(const pkv_batch_meta* meta, int32_t mode, int64_t n_slots,
+                             int64_t total_q, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

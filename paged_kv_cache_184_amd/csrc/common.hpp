@@ -1,0 +1,108 @@
+// Device helpers shared by the pkv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr int kSplitAlign = 16;  // PKV_SPLIT_ALIGN
+
+// Storage tags: bf16 is carried as raw 16-bit patterns.
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct elem_size;
+template <>
+struct elem_size<float> {
+  static constexpr int value = 4;
+};
+template <>
+struct elem_size<bf16_t> {
+  static constexpr int value = 2;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// dot of two packed bf16 pairs accumulated into fp32 (v_dot2_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves within rows of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i within 8
+constexpr int kRowMirror = 0x140;   // row_mirror: lane i <-> 15-i within 16
+constexpr int kRowRor8 = 0x128;     // row_ror:8: lane i <- lane (i+8) mod 16
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the
+// same bits (each step adds a commutative pair).
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kHalfMirror>(x);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Split rule of pkv_split_cfg: returns S (0 when L <= 0) and the chunk length.
+__host__ __device__ __forceinline__ int split_count(int L, int max_splits, int fixed_splits,
+                                                    int split_tokens, int* chunk_out) {
+  if (L <= 0) {
+    *chunk_out = 0;
+    return 0;
+  }
+  int req = fixed_splits > 0 ? fixed_splits : ceil_div(L, split_tokens);
+  req = req < 1 ? 1 : (req > max_splits ? max_splits : req);
+  int chunk = ceil_div(ceil_div(L, req), kSplitAlign) * kSplitAlign;
+  *chunk_out = chunk;
+  return ceil_div(L, chunk);
+}
+
+__device__ __forceinline__ int clamp_index(int x, int n) {
+  // maps any int to [0, n): negatives to 0, too-large to n - 1
+  return x < 0 ? 0 : (x >= n ? n - 1 : x);
+}
+
+}  // namespace pkv

@@ -1,0 +1,74 @@
+// Host-side launchers shared between the C-ABI layer (api.cpp) and the kernel
+// translation units. Arguments are already validated when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv {
+
+struct DecodeArgs {
+  const void* k;  // layer base of the K pool (already offset by layer)
+  const void* v;
+  int64_t n_slots;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t n_q_heads;
+  const void* q;
+  const int32_t* req_to_token;
+  int64_t stride;
+  int32_t n_rows;
+  int32_t batch;
+  const int32_t* req_pool_indices;
+  const int32_t* seq_lens;
+  float scale;
+  pkv_split_cfg split;
+  float* o_part;
+  float* ml_part;
+  void* out;
+};
+
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
+hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
+                           const void* k_new, const void* v_new, const int32_t* loc,
+                           int64_t n_tokens, hipStream_t stream);
+
+hipError_t launch_metadata(const pkv_batch_meta& m, int32_t mode, pkv_split_cfg split,
+                           int32_t* kv_indptr_out, int32_t* loc_out, int64_t loc_capacity,
+                           int32_t* splits_out, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* k;  // layer base
+  const void* v;
+  int64_t n_slots;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t n_q_heads;
+  const void* q;
+  const int32_t* req_to_token;
+  int64_t stride;
+  int32_t n_rows;
+  int32_t batch;
+  const int32_t* req_pool_indices;
+  const int32_t* seq_lens;
+  const int32_t* qo_indptr;
+  int32_t total_q;
+  int32_t max_q_len;
+  float scale;
+  int32_t causal;
+  void* out;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// Supported group sizes / head dims (the dispatch tables in the kernels match these).
+inline bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+inline bool head_dim_supported(int d) { return d == 64 || d == 128; }
+
+}  // namespace pkv

@@ -1,0 +1,51 @@
+// kv_store (a2): write new K/V rows at cache locations, bit-exact.
+//
+// AstrAI commit 398e8a3e page, bullets on single advanced indexing
+// buffer[layer_id, loc] and on the 4D KVStorage layout: the new token t's
+// [n_kv_heads, head_dim] row goes to pool[layer, loc[t]] for K and for V.
+// Each thread moves one 16-byte chunk of K and the same chunk of V; a row is
+// n_kv_heads * head_dim * elem bytes (2 KiB for 8 bf16 heads of 128), so a
+// token's chunks are contiguous on both sides and every access is a coalesced
+// 16-byte load/store. Locations outside [0, n_slots) are skipped.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+namespace {
+
+__global__ __launch_bounds__(256) void kv_store_kernel(char* __restrict__ k, char* __restrict__ v,
+                                                       int64_t n_slots, int64_t row_bytes,
+                                                       int64_t chunks, const char* __restrict__ kn,
+                                                       const char* __restrict__ vn,
+                                                       const int32_t* __restrict__ loc,
+                                                       int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t t = idx / chunks;
+  const int64_t ch = idx - t * chunks;
+  const int64_t slot = loc[t];
+  if (slot < 0 || slot >= n_slots) return;
+  const int64_t src = t * row_bytes + ch * 16;
+  const int64_t dst = slot * row_bytes + ch * 16;
+  const u32x4 a = *(const u32x4*)(kn + src);
+  const u32x4 b = *(const u32x4*)(vn + src);
+  *(u32x4*)(k + dst) = a;
+  *(u32x4*)(v + dst) = b;
+}
+
+}  // namespace
+
+hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
+                           const void* k_new, const void* v_new, const int32_t* loc,
+                           int64_t n_tokens, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t chunks = row_bytes / 16;
+  const int64_t total = n_tokens * chunks;
+  const int64_t blocks = (total + 255) / 256;
+  kv_store_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(
+      (char*)k_layer, (char*)v_layer, n_slots, row_bytes, chunks, (const char*)k_new,
+      (const char*)v_new, loc, total);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

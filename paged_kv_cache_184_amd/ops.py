@@ -1,0 +1,262 @@
+"""Python binding of libpkv: the C entry points of include/pkv.h under the same
+names without the ``pkv_`` prefix.
+
+Argument marshalling only: torch tensors are turned into device pointers and
+descriptors, and the current HIP stream is passed through. Every step of the
+computation runs in the library's HIP kernels; there is no Python or CPU
+fallback, and a missing library raises ``LibraryMissing``.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import BatchMeta, KVPool, SplitCfg, LibraryMissing  # noqa: F401
+
+PKV_MODE_DECODE = _lib.PKV_MODE_DECODE
+PKV_MODE_PREFILL = _lib.PKV_MODE_PREFILL
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+        self.message = message
+
+
+def lib():
+    return _lib.load()
+
+
+def _check(status: int) -> None:
+    if status != _lib.PKV_OK:
+        L = lib()
+        raise PkvError(status, L.pkv_status_str(status).decode(), L.pkv_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _lib.PKV_BF16
+    if dtype == torch.float32:
+        return _lib.PKV_F32
+    raise TypeError(f"unsupported dtype {dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor) -> KVPool:
+    """Descriptor of two contiguous [n_layers, n_slots, n_kv_heads, head_dim] pools."""
+    _need(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pools must be equal 4D tensors")
+    _need(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
+    _need(k_pool.dtype == v_pool.dtype, "K and V pools must share a dtype")
+    n_layers, n_slots, hkv, d = k_pool.shape
+    pool = KVPool(k_pool.data_ptr(), v_pool.data_ptr(), n_layers, n_slots, hkv, d,
+                  dtype_code(k_pool.dtype), 0)
+    pool._tensors = (k_pool, v_pool)  # the descriptor holds raw pointers: keep them alive
+    return pool
+
+
+def make_meta(req_to_token: torch.Tensor, req_pool_indices: torch.Tensor, seq_lens: torch.Tensor,
+              qo_indptr: Optional[torch.Tensor] = None,
+              kv_indptr: Optional[torch.Tensor] = None) -> BatchMeta:
+    """Descriptor of the int32 batch metadata (all device tensors)."""
+    for name, t in (("req_to_token", req_to_token), ("req_pool_indices", req_pool_indices),
+                    ("seq_lens", seq_lens), ("qo_indptr", qo_indptr), ("kv_indptr", kv_indptr)):
+        if t is not None:
+            _need(t.dtype == torch.int32, f"{name} must be int32")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+    _need(req_to_token.dim() == 2, "req_to_token must be 2D")
+    _need(req_pool_indices.shape[0] == seq_lens.shape[0], "req_pool_indices / seq_lens length")
+    _need(qo_indptr is None or qo_indptr.shape[0] == seq_lens.shape[0] + 1, "qo_indptr length")
+    meta = BatchMeta(req_to_token.data_ptr(), req_to_token.stride(0), req_to_token.shape[0],
+                     seq_lens.shape[0], req_pool_indices.data_ptr(), seq_lens.data_ptr(),
+                     _ptr(qo_indptr), _ptr(kv_indptr))
+    # the descriptor holds raw pointers: keep the tensors alive as long as it lives
+    meta._tensors = (req_to_token, req_pool_indices, seq_lens, qo_indptr, kv_indptr)
+    return meta
+
+
+def split_cfg(max_splits: int, fixed_splits: int = 0, split_tokens: int = 256) -> SplitCfg:
+    return SplitCfg(max_splits, fixed_splits, split_tokens, 0)
+
+
+# ----------------------------------------------------------------- entry points
+
+def abi_version() -> int:
+    return lib().pkv_abi_version()
+
+
+def kv_store(k_pool, v_pool, layer: int, k_new, v_new, loc, stream=None) -> None:
+    """pool[layer, loc[t]] = new[t] for K and V (pkv_kv_store)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "dtype mismatch")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
+    _need(loc.dtype == torch.int32 and loc.is_contiguous(), "loc must be contiguous int32")
+    n = loc.shape[0]
+    _need(k_new.numel() == n * k_pool.shape[2] * k_pool.shape[3], "k_new shape")
+    _need(v_new.numel() == k_new.numel(), "v_new shape")
+    _check(lib().pkv_kv_store(C.byref(pool), layer, k_new.data_ptr(), v_new.data_ptr(),
+                              loc.data_ptr(), n, _stream(stream)))
+
+
+def build_metadata(meta: BatchMeta, mode: int, split: Optional[SplitCfg] = None,
+                   kv_indptr_out=None, loc_out=None, splits_out=None, stream=None) -> None:
+    """Index step (pkv_build_metadata)."""
+    split = split or split_cfg(1)
+    cap = 0 if loc_out is None else loc_out.numel()
+    _check(lib().pkv_build_metadata(C.byref(meta), mode, split, _ptr(kv_indptr_out),
+                                    _ptr(loc_out), cap, _ptr(splits_out), _stream(stream)))
+
+
+def decode_workspace_bytes(batch: int, n_q_heads: int, head_dim: int, max_splits: int) -> int:
+    return int(lib().pkv_decode_workspace_bytes(batch, n_q_heads, head_dim, max_splits))
+
+
+def alloc_decode_workspace(batch: int, n_q_heads: int, head_dim: int, max_splits: int,
+                           device="cuda") -> torch.Tensor:
+    """A byte tensor big enough for pkv_decode_workspace_bytes (plain tensor even
+    under an inference-mode caller, so later in-place use from other threads works)."""
+    n = decode_workspace_bytes(batch, n_q_heads, head_dim, max_splits)
+    _need(n > 0, "invalid workspace arguments")
+    with torch.inference_mode(False):
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def workspace_views(ws: torch.Tensor, batch: int, n_q_heads: int, head_dim: int, max_splits: int):
+    """(o_part, ml_part) fp32 views of a decode workspace, in the layout pkv.h documents."""
+    o_elems = batch * n_q_heads * max_splits * head_dim
+    ml_off = (o_elems * 4 + 255) // 256 * 256
+    f = ws.view(torch.float32)
+    o = f[:o_elems].view(batch, n_q_heads, max_splits, head_dim)
+    ml = f[ml_off // 4: ml_off // 4 + batch * n_q_heads * max_splits * 2].view(
+        batch, n_q_heads, max_splits, 2)
+    return o, ml
+
+
+def _q_check(q, pool: KVPool, batch_rows: int):
+    _need(q.is_contiguous(), "q must be contiguous")
+    _need(q.dim() == 3 and q.shape[0] == batch_rows and q.shape[2] == pool.head_dim, "q shape")
+    _need(dtype_code(q.dtype) == pool.dtype, "q dtype must match the pools")
+
+
+def paged_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float,
+                      split: SplitCfg, workspace: torch.Tensor, out=None, stream=None):
+    """Split-KV paged decode (pkv_paged_decode_attn). q: [B, Hq, D]."""
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype, "out")
+    _check(lib().pkv_paged_decode_attn(C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                                       C.byref(meta), scale, split, workspace.data_ptr(),
+                                       workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_partials(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float,
+                    split: SplitCfg, workspace: torch.Tensor, stream=None) -> None:
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    _check(lib().pkv_decode_partials(C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                                     C.byref(meta), scale, split, workspace.data_ptr(),
+                                     workspace.numel(), _stream(stream)))
+
+
+def decode_merge(meta: BatchMeta, n_q_heads: int, head_dim: int, dtype: torch.dtype,
+                 split: SplitCfg, workspace: torch.Tensor, out: torch.Tensor, stream=None):
+    _check(lib().pkv_decode_merge(C.byref(meta), n_q_heads, head_dim, dtype_code(dtype), split,
+                                  workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+                                  _stream(stream)))
+    return out
+
+
+def paged_prefill_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, max_q_len: int,
+                       scale: float, causal: bool = True, out=None, stream=None):
+    """Ragged packed paged prefill (pkv_paged_prefill_attn). q: [T_q, Hq, D]."""
+    pool = make_pool(k_pool, v_pool)
+    _need(q.is_contiguous() and q.dim() == 3 and q.shape[2] == pool.head_dim, "q shape")
+    _need(dtype_code(q.dtype) == pool.dtype, "q dtype must match the pools")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype, "out")
+    _check(lib().pkv_paged_prefill_attn(C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                                        C.byref(meta), q.shape[0], max_q_len, scale,
+                                        1 if causal else 0, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def validate_meta(meta: BatchMeta, mode: int, n_slots: int, total_q: int = 0, stream=None) -> None:
+    """Synchronous debug check of the metadata contents (pkv_validate_meta)."""
+    _check(lib().pkv_validate_meta(C.byref(meta), mode, n_slots, total_q, _stream(stream)))
+
+
+class PreparedCall:
+    """A C entry point with its arguments marshalled once, for tight loops and
+    graph capture: ``call()`` re-issues the same launch (same pointers, stream)."""
+
+    def __init__(self, fn_name: str, *args, keep=()):
+        self._fn = getattr(lib(), fn_name)
+        self._args = args
+        self._keep = keep  # keeps descriptor structs alive
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, workspace, out,
+                   stream=None, stage="all"):
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    s = _stream(stream)
+    if stage == "all":
+        return PreparedCall("pkv_paged_decode_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                            C.byref(meta), scale, split, workspace.data_ptr(), workspace.numel(),
+                            out.data_ptr(), s, keep=(pool, meta))
+    if stage == "partials":
+        return PreparedCall("pkv_decode_partials", C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                            C.byref(meta), scale, split, workspace.data_ptr(), workspace.numel(), s,
+                            keep=(pool, meta))
+    if stage == "merge":
+        return PreparedCall("pkv_decode_merge", C.byref(meta), q.shape[1], pool.head_dim, pool.dtype,
+                            split, workspace.data_ptr(), workspace.numel(), out.data_ptr(), s,
+                            keep=(pool, meta))
+    raise ValueError(stage)
+
+
+def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None):
+    pool = make_pool(k_pool, v_pool)
+    return PreparedCall("pkv_kv_store", C.byref(pool), layer, k_new.data_ptr(), v_new.data_ptr(),
+                        loc.data_ptr(), loc.shape[0], _stream(stream), keep=(pool,))
+
+
+def prepare_metadata(meta: BatchMeta, mode, split, kv_indptr_out=None, loc_out=None,
+                     splits_out=None, stream=None):
+    cap = 0 if loc_out is None else loc_out.numel()
+    return PreparedCall("pkv_build_metadata", C.byref(meta), mode, split or split_cfg(1),
+                        _ptr(kv_indptr_out), _ptr(loc_out), cap, _ptr(splits_out),
+                        _stream(stream), keep=(meta,))
+
+
+def prepare_prefill(q, k_pool, v_pool, layer, meta: BatchMeta, max_q_len, scale, causal, out,
+                    stream=None):
+    pool = make_pool(k_pool, v_pool)
+    return PreparedCall("pkv_paged_prefill_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                        C.byref(meta), q.shape[0], max_q_len, scale, 1 if causal else 0,
+                        out.data_ptr(), _stream(stream), keep=(pool, meta))

@@ -1,0 +1,198 @@
+"""The C-ABI library loads, exports every symbol include/pkv.h declares, and
+rejects bad host-visible arguments before touching the GPU. CPU only: every
+call here fails validation, which returns before any HIP call."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_184_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from paged_kv_cache_184_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_matches_binding():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_info_calls(lib):
+    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_status_str(_lib.PKV_EWORKSPACE) == b"PKV_EWORKSPACE"
+    assert lib.pkv_status_str(99) == b"PKV_UNKNOWN"
+
+
+def test_workspace_bytes(lib):
+    f = lib.pkv_decode_workspace_bytes
+    # o_part 1*32*128*128*4 = 2 MiB; ml_part 1*32*128*2*4 = 32 KiB
+    assert f(1, 32, 128, 128) == 2 * 1024 * 1024 + 32 * 1024
+    # o_part of 3*5*7*64*4 = 26880 B (= 105 * 256); ml 3*5*7*8 = 840 B -> 1024
+    assert f(3, 5, 64, 7) == 26880 + 1024
+    # o_part 1*1*1*64*4 = 256; ml 8 -> 256
+    assert f(1, 1, 64, 1) == 512
+    assert f(0, 32, 128, 1) == 0
+    assert f(1, 32, 128, 0) == 0
+    assert f(1, 32, 128, _lib.PKV_MAX_SPLITS + 1) == 0
+    # monotone in batch: a workspace for B serves any smaller batch
+    assert all(f(b, 8, 128, 16) <= f(b + 1, 8, 128, 16) for b in range(1, 40))
+
+
+def _pool(**kw):
+    base = dict(k=16, v=32, n_layers=2, n_slots=64, n_kv_heads=2, head_dim=64,
+                dtype=_lib.PKV_BF16, reserved=0)
+    base.update(kw)
+    return _lib.KVPool(**base)
+
+
+def _meta(**kw):
+    base = dict(req_to_token=16, req_to_token_stride=8, n_req_rows=2, batch=1,
+                req_pool_indices=32, seq_lens=48, qo_indptr=None, kv_indptr=None)
+    base.update(kw)
+    return _lib.BatchMeta(**base)
+
+
+def _split(max_splits=4, fixed=0, tokens=16):
+    return _lib.SplitCfg(max_splits, fixed, tokens, 0)
+
+
+@pytest.mark.parametrize("pool_kw,layer,code", [
+    (dict(dtype=7), 0, _lib.PKV_EDTYPE),
+    (dict(k=None), 0, _lib.PKV_EINVAL),
+    (dict(head_dim=96), 0, _lib.PKV_EUNSUPPORTED),
+    (dict(n_slots=0), 0, _lib.PKV_ESHAPE),
+    (dict(), 2, _lib.PKV_EINVAL),
+    (dict(), -1, _lib.PKV_EINVAL),
+    (dict(k=24), 0, _lib.PKV_EALIGN),
+])
+def test_kv_store_rejects(lib, pool_kw, layer, code):
+    p = _pool(**pool_kw)
+    st = lib.pkv_kv_store(C.byref(p), layer, 16, 16, 16, 1, None)
+    assert st == code, lib.pkv_last_error()
+    assert lib.pkv_last_error() != b""
+
+
+def test_kv_store_other_rejects(lib):
+    p = _pool()
+    assert lib.pkv_kv_store(None, 0, 16, 16, 16, 1, None) == _lib.PKV_EINVAL
+    assert lib.pkv_kv_store(C.byref(p), 0, 16, 16, 16, -1, None) == _lib.PKV_EINVAL
+    assert lib.pkv_kv_store(C.byref(p), 0, 17, 16, 16, 1, None) == _lib.PKV_EALIGN
+    assert lib.pkv_kv_store(C.byref(p), 0, None, 16, 16, 1, None) == _lib.PKV_EINVAL
+    # zero tokens is a successful no-op with nothing launched
+    assert lib.pkv_kv_store(C.byref(p), 0, None, None, None, 0, None) == _lib.PKV_OK
+    assert lib.pkv_last_error() == b""
+
+
+def _decode(lib, pool=None, layer=0, q=16, hq=4, meta=None, scale=0.125, split=None, ws=256,
+            ws_bytes=1 << 20, out=16, fn="pkv_paged_decode_attn"):
+    pool = pool or _pool()
+    meta = meta or _meta()
+    split = split or _split()
+    if fn == "pkv_paged_decode_attn":
+        return lib.pkv_paged_decode_attn(C.byref(pool), layer, q, hq, C.byref(meta), scale, split,
+                                         ws, ws_bytes, out, None)
+    return lib.pkv_decode_partials(C.byref(pool), layer, q, hq, C.byref(meta), scale, split, ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["pkv_paged_decode_attn", "pkv_decode_partials"])
+def test_decode_rejects(lib, fn):
+    E = _lib
+    assert _decode(lib, hq=3, fn=fn) == E.PKV_ESHAPE  # 3 % 2 != 0
+    assert _decode(lib, hq=64, fn=fn) == E.PKV_EUNSUPPORTED  # group 32
+    assert _decode(lib, hq=0, fn=fn) == E.PKV_ESHAPE
+    assert _decode(lib, q=20, fn=fn) == E.PKV_EALIGN
+    assert _decode(lib, q=None, fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, ws=None, fn=fn) == E.PKV_EWORKSPACE
+    assert _decode(lib, ws=128, fn=fn) == E.PKV_EALIGN
+    assert _decode(lib, ws_bytes=100, fn=fn) == E.PKV_EWORKSPACE
+    assert _decode(lib, scale=float("nan"), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, scale=float("inf"), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, split=_split(max_splits=0), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, split=_split(max_splits=E.PKV_MAX_SPLITS + 1), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, split=_split(tokens=24), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, split=_split(tokens=0), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, split=_split(fixed=-1), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, meta=_meta(batch=-1), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, meta=_meta(batch=70000), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, meta=_meta(seq_lens=None), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, meta=_meta(req_to_token_stride=0), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, meta=_meta(n_req_rows=0), fn=fn) == E.PKV_EINVAL
+    assert _decode(lib, pool=_pool(dtype=3), fn=fn) == E.PKV_EDTYPE
+    assert _decode(lib, layer=5, fn=fn) == E.PKV_EINVAL
+    if fn == "pkv_paged_decode_attn":
+        assert _decode(lib, out=None, fn=fn) == E.PKV_EINVAL
+        assert _decode(lib, out=40, fn=fn) == E.PKV_EALIGN
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, meta=_meta(batch=0), q=None, ws=None, out=None) == _lib.PKV_OK
+
+
+def test_merge_rejects(lib):
+    E = _lib
+    m = _meta()
+    s = _split()
+    f = lib.pkv_decode_merge
+    assert f(C.byref(m), 4, 64, 9, s, 256, 1 << 20, 16, None) == E.PKV_EDTYPE
+    assert f(C.byref(m), 4, 80, 1, s, 256, 1 << 20, 16, None) == E.PKV_EUNSUPPORTED
+    assert f(C.byref(m), 4, 64, 1, s, 256, 10, 16, None) == E.PKV_EWORKSPACE
+    assert f(C.byref(m), 4, 64, 1, s, 264, 1 << 20, 16, None) == E.PKV_EALIGN
+    assert f(C.byref(m), 4, 64, 1, s, 256, 1 << 20, None, None) == E.PKV_EINVAL
+
+
+def test_metadata_rejects(lib):
+    E = _lib
+    m = _meta()
+    s = _split()
+    f = lib.pkv_build_metadata
+    assert f(C.byref(m), 5, s, 16, None, 0, None, None) == E.PKV_EINVAL
+    assert f(C.byref(m), E.PKV_MODE_PREFILL, s, 16, None, 0, None, None) == E.PKV_EINVAL  # no qo
+    mq = _meta(qo_indptr=64)
+    assert f(C.byref(mq), E.PKV_MODE_PREFILL, s, None, None, 0, 16, None) == E.PKV_EINVAL
+    assert f(C.byref(m), E.PKV_MODE_DECODE, s, None, 16, 0, None, None) == E.PKV_EINVAL  # cap<B
+    assert f(C.byref(m), E.PKV_MODE_DECODE, _split(max_splits=0), None, None, 0, 16,
+             None) == E.PKV_EINVAL
+    # nothing requested: success without a launch
+    assert f(C.byref(m), E.PKV_MODE_DECODE, s, None, None, 0, None, None) == E.PKV_OK
+
+
+def test_prefill_rejects(lib):
+    E = _lib
+    p = _pool()
+    m = _meta(qo_indptr=64)
+    f = lib.pkv_paged_prefill_attn
+    assert f(C.byref(p), 0, 16, 4, C.byref(_meta()), 4, 4, 0.1, 1, 16, None) == E.PKV_EINVAL
+    assert f(C.byref(p), 0, 16, 4, C.byref(m), -1, 4, 0.1, 1, 16, None) == E.PKV_EINVAL
+    assert f(C.byref(p), 0, 16, 4, C.byref(m), 4, 4, 0.1, 2, 16, None) == E.PKV_EINVAL
+    assert f(C.byref(p), 0, 24, 4, C.byref(m), 4, 4, 0.1, 1, 16, None) == E.PKV_EALIGN
+    assert f(C.byref(p), 0, 16, 5, C.byref(m), 4, 4, 0.1, 1, 16, None) == E.PKV_ESHAPE
+    assert f(C.byref(p), 0, 16, 6, C.byref(m), 4, 4, 0.1, 1, 16, None) == E.PKV_EUNSUPPORTED
+    assert f(C.byref(_pool(dtype=_lib.PKV_F32)), 0, 16, 4, C.byref(m), 4, 4, 0.1, 1, 16,
+             None) == E.PKV_EUNSUPPORTED
+    assert f(C.byref(p), 0, 16, 4, C.byref(m), 0, 0, 0.1, 1, 16, None) == E.PKV_OK  # empty
+
+
+def test_validate_meta_rejects(lib):
+    assert lib.pkv_validate_meta(C.byref(_meta()), 3, 10, 0, None) == _lib.PKV_EINVAL
+    assert lib.pkv_validate_meta(None, 0, 10, 0, None) == _lib.PKV_EINVAL
