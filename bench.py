@@ -42,9 +42,32 @@ def parse():
     p.add_argument("--headline", type=int, default=32768)
     p.add_argument("--split-tokens", type=int, default=256)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="also time HIP-graph replay")
+    p.add_argument("--profile", action="store_true",
+                   help="short run for hardware counters: a 256 MiB device copy (counter "
+                        "calibration) then a few decode steps of the headline workload")
     return p.parse_args()
+
+
+def profile_run(args):
+    """A plain device-to-device copy of known size, then a few steps: the copy
+    gives the scale of FETCH_SIZE / WRITE_SIZE for bytes actually moved."""
+    import torch
+
+    n = 256 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    db = DecodeBench(args.headline, n_layers=8, split_tokens=args.split_tokens, seed=184_002)
+    for i in range(max(8, args.steps)):
+        db.step(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": "done", "copy_bytes": n, "steps": max(8, args.steps),
+                      "partial_kernel_bytes": db.partial_kernel_bytes()}), flush=True)
 
 
 _SPIN_RATE = None
@@ -232,6 +255,89 @@ class DecodeBench:
                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+
+class PrefillBench:
+    """Packed ragged paged prefill: 8 requests, 64..2048 new tokens each over a
+    0..4096-token cached prefix, 32 q / 8 KV heads, head_dim 128, bf16, causal.
+    A step is the index step (new-token locations), the store of the new
+    tokens' K/V and the MFMA prefill kernel, rotating over 8 layers."""
+
+    def __init__(self, n_layers: int, seed: int):
+        import torch
+
+        from paged_kv_cache_184_amd import ops
+        from paged_kv_cache_184_amd import workloads as W
+
+        self.torch = torch
+        b = W.packed_prefill(n_layers=n_layers)
+        self.b = b
+        dev = "cuda"
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        shape = (b.n_layers, b.n_slots, b.n_kv_heads, b.head_dim)
+        self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+        live = torch.from_numpy(b.live_slots).to(dev).long()
+        kv = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
+        kv = kv.to(torch.bfloat16)
+        for layer in range(b.n_layers):
+            self.k_pool[layer, live] = kv[0]
+            self.v_pool[layer, live] = kv[1]
+        del kv
+        T = b.total_q
+        self.q = torch.randn((T, b.n_q_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.k_new = torch.randn((T, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.v_new = torch.randn((T, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
+        self.r2t = torch.from_numpy(b.req_to_token).to(dev)
+        self.rows = torch.from_numpy(b.req_pool_indices).to(dev)
+        self.lens = torch.from_numpy(b.seq_lens).to(dev)
+        self.qo = torch.from_numpy(b.qo_indptr).to(dev)
+        self.meta = ops.make_meta(self.r2t, self.rows, self.lens, self.qo)
+        self.loc = torch.empty(T, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.q)
+        self.calls = []
+        for layer in range(b.n_layers):
+            self.calls.append((
+                ops.prepare_metadata(self.meta, ops.PKV_MODE_PREFILL, None, None, self.loc, None),
+                ops.prepare_kv_store(self.k_pool, self.v_pool, layer, self.k_new, self.v_new,
+                                     self.loc),
+                ops.prepare_prefill(self.q, self.k_pool, self.v_pool, layer, self.meta,
+                                    b.max_q_len, b.scale, True, self.out),
+            ))
+
+    def flops(self) -> float:
+        b = self.b
+        n = b.n_new.astype(np.float64)
+        P = (b.seq_lens - b.n_new).astype(np.float64)
+        return float(4 * b.head_dim * b.n_q_heads * np.sum(n * P + n * (n + 1) / 2))
+
+    def run(self, steps: int, warmup: int):
+        torch = self.torch
+        for i in range(warmup):
+            for c in self.calls[i % len(self.calls)]:
+                c()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            meta_call, store_call, attn_call = self.calls[i % len(self.calls)]
+            meta_call()
+            store_call()
+            evs[i][0].record()
+            attn_call()
+            evs[i][1].record()
+        end.record()
+        torch.cuda.synchronize()
+        step_ms = start.elapsed_time(end) / steps
+        attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return step_ms, attn_ms
+
+
 def cpu_baseline(db: DecodeBench, seconds: float):
     """Time the fp64 oracle on the headline workload until ``seconds`` of CPU
     work have run; report KV GB/s in the same unit as the GPU."""
@@ -247,7 +353,7 @@ def cpu_baseline(db: DecodeBench, seconds: float):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        O.decode_attention(*args[:4], args[4], args[5], args[6])
+        O.decode_attention(args[0], args[1], args[2], 0, args[3], args[4], args[5], args[6])
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -266,6 +372,9 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile:
+        profile_run(args)
+        return
     detail = {}
     head = None
     for ctx in args.ctx:
@@ -292,6 +401,18 @@ def main():
         else:
             del db
             torch.cuda.empty_cache()
+    if not args.no_prefill:
+        pb = PrefillBench(n_layers=8, seed=184_004)
+        p_step, p_attn = pb.run(max(10, args.steps // 5), 3)
+        tflops = pb.flops() / (p_attn * 1e-3) / 1e12
+        detail["prefill"] = {
+            "workload": "packed_prefill (8 requests, T_q=%d)" % pb.b.total_q,
+            "us_per_step": round(p_step * 1e3, 1), "kernel_us": round(p_attn * 1e3, 1),
+            "gflop": round(pb.flops() / 1e9, 1), "tflops": round(tflops, 1),
+            "mfma_util_pct": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 1)}
+        print(f"# prefill: {detail['prefill']}", file=sys.stderr, flush=True)
+        del pb
+        torch.cuda.empty_cache()
     if head is None:
         raise SystemExit("--headline must be one of --ctx")
     db, step_ms, part_ms, host_s = head

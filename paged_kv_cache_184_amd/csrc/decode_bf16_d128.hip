@@ -1,0 +1,15 @@
+// Decode kernel instantiations for bf16 K/V, head_dim 128
+// (one translation unit per variant so the library builds in parallel).
+#include "decode_impl.hpp"
+
+namespace pkv {
+
+hipError_t launch_decode_partials_bf16_128(const DecodeArgs& a, hipStream_t stream) {
+  return decode_impl::partials_for_dim<bf16_t, 128>(a, stream);
+}
+
+hipError_t launch_decode_merge_bf16_128(const DecodeArgs& a, hipStream_t stream) {
+  return decode_impl::merge_for_dim<bf16_t, 128>(a, stream);
+}
+
+}  // namespace pkv

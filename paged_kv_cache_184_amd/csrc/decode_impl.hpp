@@ -1,0 +1,440 @@
+// Split-KV paged decode attention for gfx950: partial kernel (a3) and
+// log-sum-exp merge (a4). Instantiated per (dtype, head_dim) in the
+// decode_*.hip translation units.
+//
+// Source passages (AstrAI pages): decode writes split partials into
+// workspace-owned o_part / "ml" buffers that a merge combines (commit 398e8a3e,
+// bullets on decode_o_part / decode_ml_part and on pre-allocated partials);
+// K/V are read through the req_to_token slot table instead of a gathered copy
+// (same page, bullet on removing Storage.gather); int32 indices (same page).
+//
+// Partial kernel: one workgroup of kWaves waves per (request b, KV head, split
+// s); each wave takes a contiguous quarter of the split's tokens.
+//   * Lanes form 8 groups of 8; group t handles tokens t and t+8 of a 16-token
+//     tile, lane c of the group holds 16-byte chunks c, c+8, ... of the
+//     token's K and V rows (D*es bytes per (slot, KV head)), so every load is a
+//     coalesced 16-byte gather and 8 lanes cover one row with full 128-byte
+//     segments.
+//   * All g = Hq/Hkv query heads of the KV head are processed by the same wave,
+//     so each K/V byte is fetched from HBM once per request and reused g times
+//     from registers.
+//   * q.k: v_dot2_f32_bf16 on packed bf16 pairs (fp32 accumulate), then a
+//     3-step DPP reduction inside the 8-lane group.
+//   * Online softmax in base 2 with a wave-uniform stabiliser m per head that
+//     is raised only when some score exceeds it by more than kTau (log2 units):
+//     until then exp2(x - m) <= 2^kTau, so no rescale of the accumulators is
+//     needed on most tiles. The final o / l does not depend on m.
+//   * Slot ids are staged per 128-token super-tile into LDS (the next
+//     super-tile's ids are prefetched into registers), so the K/V gathers
+//     depend on an LDS read only. A super-tile is straight-line code (one
+//     instantiation per tile count) with three tile buffers: each tile's loads
+//     are issued two tiles ahead of its use and no buffer is carried around a
+//     loop, which keeps the hardware wait counts static.
+//   * Tokens past the range end read its last valid token (clamped position)
+//     and get p = 0, so padding slots are never read.
+//   * The kWaves partial states are merged in LDS in a fixed order.
+// The reduction order depends only on the logical token position, so results
+// are bit-identical across runs and across slot relocations.
+#pragma once
+
+#include <math.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pkv {
+namespace decode_impl {
+
+constexpr float kTau = 8.0f;  // log2 headroom before the stabiliser is raised
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T, int D>
+struct Geo {
+  static constexpr int ES = elem_size<T>::value;
+  static constexpr int ROW = D * ES;          // bytes of one (slot, KV head) row
+  static constexpr int CH = ROW / (8 * 16);  // 16-byte chunks per lane per token
+  static constexpr int EPC = 16 / ES;        // elements per chunk
+  static constexpr int E = CH * EPC;         // elements per lane per token (D / 8)
+  static_assert(CH >= 1 && CH <= 4, "row size");
+};
+
+template <typename T, int D>
+struct TileBuf {
+  u32x4 k[2][Geo<T, D>::CH];
+  u32x4 v[2][Geo<T, D>::CH];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(TileBuf<T, D>& buf, const char* kbase, const char* vbase,
+                                          int64_t row_stride, const int slot[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t off = (int64_t)slot[j] * row_stride;
+#pragma unroll
+    for (int k = 0; k < Geo<T, D>::CH; ++k) {
+      buf.k[j][k] = *(const u32x4*)(kbase + off + 128 * k);
+      buf.v[j][k] = *(const u32x4*)(vbase + off + 128 * k);
+    }
+  }
+}
+
+// Partial dot product of this lane's elements of q (head h) and k.
+template <typename T, int D>
+__device__ __forceinline__ float lane_dot(const u32x4 (&q)[Geo<T, D>::CH],
+                                          const u32x4 (&k)[Geo<T, D>::CH]) {
+  float acc = 0.f;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int c = 0; c < Geo<T, D>::CH; ++c) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc = dot2_bf16(q[c][w], k[c][w], acc);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < Geo<T, D>::CH; ++c) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(q[c][w]), __uint_as_float(k[c][w]), acc);
+    }
+  }
+  return acc;
+}
+
+// Element e (0..E-1) of a lane's row chunk set, as fp32.
+template <typename T, int D>
+__device__ __forceinline__ float elem(const u32x4 (&r)[Geo<T, D>::CH], int e) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w = r[e / 8][(e % 8) / 2];
+    return (e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w);
+  } else {
+    return __uint_as_float(r[e / 4][e % 4]);
+  }
+}
+
+template <typename T, int D, int G>
+struct State {
+  float acc[G][Geo<T, D>::E];
+  float l[G];
+  float m[G];  // log2 units, wave-uniform
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void compute_tile(State<T, D, G>& st, const TileBuf<T, D>& buf,
+                                             const u32x4 (&q)[G][Geo<T, D>::CH], float scale2,
+                                             bool valid0, bool valid1) {
+  constexpr int E = Geo<T, D>::E;
+  float sc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    // reduce unconditionally (all lanes active for the DPP moves), then mask
+    const float x0 = sum8(lane_dot<T, D>(q[h], buf.k[0])) * scale2;
+    const float x1 = sum8(lane_dot<T, D>(q[h], buf.k[1])) * scale2;
+    sc[h][0] = valid0 ? x0 : -INFINITY;
+    sc[h][1] = valid1 ? x1 : -INFINITY;
+  }
+  bool need = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) need |= fmaxf(sc[h][0], sc[h][1]) > st.m[h] + kTau;
+  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mnew = fmaxf(st.m[h], wave_max(fmaxf(sc[h][0], sc[h][1])));
+      const float corr = __builtin_amdgcn_exp2f(st.m[h] - mnew);
+      st.l[h] *= corr;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] *= corr;
+      st.m[h] = mnew;
+    }
+  }
+  float v0[E], v1[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v0[e] = elem<T, D>(buf.v[0], e);
+    v1[e] = elem<T, D>(buf.v[1], e);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
+    const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
+    st.l[h] += p0 + p1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(p1, v1[e], fmaf(p0, v0[e], st.acc[h][e]));
+  }
+}
+
+constexpr int kWaves = 4;   // waves per workgroup; each takes a quarter of the split
+constexpr int kTiles = 8;   // 16-token tiles per super-tile (straight-line, fully unrolled)
+constexpr int kSuper = 16 * kTiles;
+
+// NT consecutive 16-token tiles starting at token cb (the last may end early at
+// ce), as straight-line code: every load is unconditional and issued two tiles
+// ahead of its use, so the wait counts are static and no tile buffer is carried
+// around a loop. Positions past ce re-read the last valid token (cache hits)
+// and are masked.
+template <typename T, int D, int G, int NT>
+__device__ __forceinline__ void tile_run(State<T, D, G>& st, const int* slots, int cb, int ce,
+                                         int grp, const char* kbase, const char* vbase,
+                                         int64_t row_stride, const u32x4 (&q)[G][Geo<T, D>::CH],
+                                         float scale2) {
+  TileBuf<T, D> buf[3];
+  auto issue = [&](int i) {
+    int sl[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sl[j] = slots[min(16 * i + grp + 8 * j, ce - cb - 1)];
+    load_tile<T, D>(buf[i % 3], kbase, vbase, row_stride, sl);
+  };
+  issue(0);
+  if (NT > 1) issue(1);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    if (i + 2 < NT) issue(i + 2);
+    const int t = cb + 16 * i + grp;
+    compute_tile<T, D, G>(st, buf[i % 3], q, scale2, t < ce, t + 8 < ce);
+  }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void super_tile(State<T, D, G>& st, const int* slots, int cb, int ce,
+                                           int grp, const char* kbase, const char* vbase,
+                                           int64_t row_stride, const u32x4 (&q)[G][Geo<T, D>::CH],
+                                           float scale2) {
+  if constexpr (sizeof(T) == 4) {
+    // fp32 inputs: one tile at a time (no cross-tile prefetch); a precision
+    // path, not a bandwidth path
+    for (int t0 = cb; t0 < ce; t0 += 16)
+      tile_run<T, D, G, 1>(st, slots + (t0 - cb), t0, ce, grp, kbase, vbase, row_stride, q, scale2);
+    return;
+  }
+  switch (ceil_div(ce - cb, 16)) {
+#define PKV_RUN(n) \
+  case n: tile_run<T, D, G, n>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2); break;
+    PKV_RUN(1) PKV_RUN(2) PKV_RUN(3) PKV_RUN(4) PKV_RUN(5) PKV_RUN(6) PKV_RUN(7) PKV_RUN(8)
+#undef PKV_RUN
+    default: break;
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * kWaves)
+void decode_partial_kernel(DecodeArgs a) {
+  using Gm = Geo<T, D>;
+  constexpr int CH = Gm::CH;
+  constexpr int E = Gm::E;
+  __shared__ int slot_lds[kWaves][kSuper];
+  __shared__ float red_acc[kWaves][G][D];
+  __shared__ float red_ml[kWaves][G][2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int grp = lane >> 3;
+  const int c = lane & 7;
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+  int chunk;
+  const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
+                            &chunk);
+  if (s >= S) return;
+  const int lo = s * chunk;
+  const int hi = min(L, lo + chunk);
+  // this wave's contiguous share of the split, a multiple of 16 tokens
+  const int sub = ceil_div(ceil_div(hi - lo, kWaves), 16) * 16;
+  const int wlo = min(hi, lo + wave * sub);
+  const int whi = min(hi, wlo + sub);
+
+  const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
+  const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
+  const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
+  const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
+  const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW + 16 * c;
+  const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW + 16 * c;
+
+  // slot ids of the first super-tile: two per lane, issued before anything waits
+  int ids[2];
+  if (wlo < whi) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ids[j] = row[min(wlo + lane + 64 * j, whi - 1)];
+  }
+
+  // q chunks of the g heads, in the same lane layout as K.
+  u32x4 q[G][CH];
+  const char* qbase = (const char*)a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G) * Gm::ROW + 16 * c;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int k = 0; k < CH; ++k) q[h][k] = *(const u32x4*)(qbase + (int64_t)h * Gm::ROW + 128 * k);
+
+  const float scale2 = a.scale * kLog2e;
+  State<T, D, G> st;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.l[h] = 0.f;
+    st.m[h] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[h][e] = 0.f;
+  }
+
+  int* slots = slot_lds[wave];
+  for (int cb = wlo; cb < whi; cb += kSuper) {
+    const int ce = min(whi, cb + kSuper);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) slots[lane + 64 * j] = clamp_index(ids[j], n_slots);
+    // other lanes of this wave read these ids: order the LDS writes first
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // prefetch the next super-tile's ids while this one runs
+    const int nb = cb + kSuper;
+    if (nb < whi) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) ids[j] = row[min(nb + lane + 64 * j, whi - 1)];
+    }
+    super_tile<T, D, G>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
+  }
+
+  // Reduce over the 8 token groups: lanes with equal c hold the same elements.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.l[h] += dpp<kRowRor8>(st.l[h]);
+    st.l[h] += __shfl_xor(st.l[h], 16);
+    st.l[h] += __shfl_xor(st.l[h], 32);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float x = st.acc[h][e];
+      x += dpp<kRowRor8>(x);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      st.acc[h][e] = x;
+    }
+  }
+  // Hand the wave's (m, l, acc) to LDS; an empty wave leaves m = -inf, l = 0, acc = 0.
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int e = 0; e < Gm::EPC; ++e)
+          red_acc[wave][h][(c + 8 * k) * Gm::EPC + e] = st.acc[h][k * Gm::EPC + e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      red_ml[wave][h][0] = st.m[h];
+      red_ml[wave][h][1] = st.l[h];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves (fixed order) and write the split's partial.
+  const int qh0 = kvh * G;
+  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits + s;
+  for (int i = tid; i < G * D; i += 64 * kWaves) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = red_ml[w][h][0];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      num = fmaf(f, red_acc[w][h][d], num);
+      den = fmaf(f, red_ml[w][h][1], den);
+    }
+    const int64_t part = part0 + (int64_t)h * a.split.max_splits;
+    a.o_part[part * D + d] = num / den;
+    if (d == 0) {
+      float2 ml;
+      ml.x = M * kLn2;
+      ml.y = den;
+      *(float2*)(a.ml_part + 2 * part) = ml;
+    }
+  }
+}
+
+// One wave per (request, q head): out = sum_s w_s o_s / sum_s w_s, reading
+// the partials eight splits at a time so their loads overlap.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;  // elements per lane
+  constexpr int U = 8;
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+  int chunk;
+  const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
+                            &chunk);
+  const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
+  const float* ml = a.ml_part + 2 * part;
+  const float* o = a.o_part + part * D + lane * PER;
+
+  // stabiliser: max of m over the splits, one split per lane, then across the wave
+  float M = -INFINITY;
+  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
+  M = wave_max(M);
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  for (int s0 = 0; s0 < S; s0 += U) {
+    float ov[U][PER], mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, S - 1);
+      mv[u] = ml[2 * s];
+      lv[u] = s0 + u < S ? ml[2 * s + 1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[u][e] = o[(int64_t)s * D + e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = lv[u] * __builtin_amdgcn_exp2f((mv[u] - M) * kLog2e);
+      den += w;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
+    }
+  }
+  const float inv = S > 0 ? 1.0f / den : 0.f;
+  const int64_t orow = ((int64_t)b * a.n_q_heads + h) * D + lane * PER;
+  if constexpr (sizeof(T) == 2) {
+    uint16_t* out = (uint16_t*)a.out + orow;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = (uint16_t)f32_to_bf16_rne(acc[e] * inv);
+  } else {
+    float* out = (float*)a.out + orow;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
+  }
+}
+
+template <typename T, int D>
+hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  dim3 grid(a.split.max_splits, a.n_kv_heads, a.batch);
+  switch (g) {
+    case 1: decode_partial_kernel<T, D, 1><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    case 2: decode_partial_kernel<T, D, 2><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    case 4: decode_partial_kernel<T, D, 4><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    case 8: decode_partial_kernel<T, D, 8><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    case 16: decode_partial_kernel<T, D, 16><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t merge_for_dim(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_q_heads, a.batch);
+  decode_merge_kernel<T, D><<<grid, 64, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace decode_impl
+}  // namespace pkv

@@ -209,14 +209,20 @@ def validate_meta(meta: BatchMeta, mode: int, n_slots: int, total_q: int = 0, st
 
 class PreparedCall:
     """A C entry point with its arguments marshalled once, for tight loops and
-    graph capture: ``call()`` re-issues the same launch (same pointers, stream)."""
+    graph capture: ``call()`` re-issues the same launch with the same pointers.
+    The last argument is the stream; when it was not fixed at preparation, the
+    current stream is looked up at call time (so calls made under a graph
+    capture land on the capturing stream)."""
 
-    def __init__(self, fn_name: str, *args, keep=()):
+    def __init__(self, fn_name: str, *args, keep=(), stream=None):
         self._fn = getattr(lib(), fn_name)
-        self._args = args
+        self._args = list(args)
+        self._stream = stream
         self._keep = keep  # keeps descriptor structs alive
 
     def __call__(self) -> None:
+        s = self._stream if self._stream is not None else torch.cuda.current_stream()
+        self._args[-1] = s.cuda_stream
         _check(self._fn(*self._args))
 
 
@@ -224,26 +230,26 @@ def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, work
                    stream=None, stage="all"):
     pool = make_pool(k_pool, v_pool)
     _q_check(q, pool, meta.batch)
-    s = _stream(stream)
+    s = None
     if stage == "all":
         return PreparedCall("pkv_paged_decode_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
                             C.byref(meta), scale, split, workspace.data_ptr(), workspace.numel(),
-                            out.data_ptr(), s, keep=(pool, meta))
+                            out.data_ptr(), s, keep=(pool, meta), stream=stream)
     if stage == "partials":
         return PreparedCall("pkv_decode_partials", C.byref(pool), layer, q.data_ptr(), q.shape[1],
                             C.byref(meta), scale, split, workspace.data_ptr(), workspace.numel(), s,
-                            keep=(pool, meta))
+                            keep=(pool, meta), stream=stream)
     if stage == "merge":
         return PreparedCall("pkv_decode_merge", C.byref(meta), q.shape[1], pool.head_dim, pool.dtype,
                             split, workspace.data_ptr(), workspace.numel(), out.data_ptr(), s,
-                            keep=(pool, meta))
+                            keep=(pool, meta), stream=stream)
     raise ValueError(stage)
 
 
 def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None):
     pool = make_pool(k_pool, v_pool)
     return PreparedCall("pkv_kv_store", C.byref(pool), layer, k_new.data_ptr(), v_new.data_ptr(),
-                        loc.data_ptr(), loc.shape[0], _stream(stream), keep=(pool,))
+                        loc.data_ptr(), loc.shape[0], None, keep=(pool,), stream=stream)
 
 
 def prepare_metadata(meta: BatchMeta, mode, split, kv_indptr_out=None, loc_out=None,
@@ -251,7 +257,7 @@ def prepare_metadata(meta: BatchMeta, mode, split, kv_indptr_out=None, loc_out=N
     cap = 0 if loc_out is None else loc_out.numel()
     return PreparedCall("pkv_build_metadata", C.byref(meta), mode, split or split_cfg(1),
                         _ptr(kv_indptr_out), _ptr(loc_out), cap, _ptr(splits_out),
-                        _stream(stream), keep=(meta,))
+                        None, keep=(meta,), stream=stream)
 
 
 def prepare_prefill(q, k_pool, v_pool, layer, meta: BatchMeta, max_q_len, scale, causal, out,
@@ -259,4 +265,4 @@ def prepare_prefill(q, k_pool, v_pool, layer, meta: BatchMeta, max_q_len, scale,
     pool = make_pool(k_pool, v_pool)
     return PreparedCall("pkv_paged_prefill_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
                         C.byref(meta), q.shape[0], max_q_len, scale, 1 if causal else 0,
-                        out.data_ptr(), _stream(stream), keep=(pool, meta))
+                        out.data_ptr(), None, keep=(pool, meta), stream=stream)
