@@ -130,7 +130,10 @@ class DecodeBench:
         self.kv_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
         self.loc = torch.empty(B, dtype=torch.int32, device=dev)
         self.splits = torch.empty(B, dtype=torch.int32, device=dev)
+        # separate path: index step, store, decode attention (merge fused inside)
         self.calls = []
+        # fused path: all four rows in one launch
+        self.fused = []
         for layer in range(b.n_layers):
             self.calls.append((
                 ops.prepare_metadata(self.meta, ops.PKV_MODE_DECODE, self.split, self.kv_indptr,
@@ -138,10 +141,13 @@ class DecodeBench:
                 ops.prepare_kv_store(self.k_pool, self.v_pool, layer, self.k_new, self.v_new,
                                      self.loc),
                 ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale,
-                                   self.split, self.ws, self.out, stage="partials"),
-                ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale,
-                                   self.split, self.ws, self.out, stage="merge"),
+                                   self.split, self.ws, self.out, stage="all"),
             ))
+            self.fused.append(ops.prepare_decode_step(
+                self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale, self.split, self.ws,
+                self.out, k_new=self.k_new, v_new=self.v_new, kv_indptr_out=self.kv_indptr,
+                loc_out=self.loc, splits_out=self.splits))
+        self.mode = "fused"
 
     # algorithmic bytes
     def kv_bytes(self) -> int:
@@ -153,19 +159,29 @@ class DecodeBench:
         return self.kv_bytes() + b.batch * b.n_q_heads * b.head_dim * 2 + L * 4
 
     def step_bytes(self) -> int:
+        """Algorithmic bytes of a whole step: K/V, q, slot ids, the output, and
+        the new token's K/V read and stored."""
         b = self.b
-        return self.partial_kernel_bytes() + b.batch * b.n_q_heads * b.head_dim * 2
+        return (self.partial_kernel_bytes() + b.batch * b.n_q_heads * b.head_dim * 2 +
+                2 * 2 * b.batch * b.n_kv_heads * b.head_dim * 2)
 
     def step(self, i: int, ev=None):
-        meta_call, store_call, part_call, merge_call = self.calls[i % len(self.calls)]
+        """One decode step for layer i mod n_layers; ev brackets the attention kernel."""
+        if self.mode == "fused":
+            if ev is not None:
+                ev[0].record()
+            self.fused[i % len(self.fused)]()
+            if ev is not None:
+                ev[1].record()
+            return
+        meta_call, store_call, attn_call = self.calls[i % len(self.calls)]
         meta_call()
         store_call()
         if ev is not None:
             ev[0].record()
-        part_call()
+        attn_call()
         if ev is not None:
             ev[1].record()
-        merge_call()
 
     def run(self, steps: int, warmup: int):
         torch = self.torch
@@ -379,14 +395,19 @@ def main():
     head = None
     for ctx in args.ctx:
         db = DecodeBench(ctx, n_layers=8, split_tokens=args.split_tokens, seed=184_002 + ctx)
+        db.mode = "separate"
+        sep_ms, sep_attn_ms, _ = db.run(args.steps, args.warmup)
+        db.mode = "fused"
         step_ms, part_ms, host_s = db.run(args.steps, args.warmup)
         err = db.check()
         entry = {
             "us_per_step": round(step_ms * 1e3, 2),
             "kv_gbs": round(db.kv_bytes() / (step_ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * db.step_bytes() / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-            "partial_kernel_us": round(part_ms * 1e3, 2),
-            "partial_kernel_gbs": round(db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9, 1),
+            "kernel_us": round(part_ms * 1e3, 2),
+            "kernel_gbs": round(db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9, 1),
+            "separate_calls_us_per_step": round(sep_ms * 1e3, 2),
+            "separate_attn_kernel_us": round(sep_attn_ms * 1e3, 2),
             "splits": int(db.split.max_splits),
             "max_abs_err": err,
         }
@@ -440,7 +461,7 @@ def main():
         "host_s_timed_region": round(host_s, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_partial_kernel<bf16,128,4>"},
+                     "kernel": "decode_partial_kernel<bf16,128,4> (fused decode step)"},
         "detail": detail,
     }
     if not args.no_cpu:

@@ -165,16 +165,19 @@ pkv_status pkv_build_metadata(const pkv_batch_meta* meta, int32_t mode, pkv_spli
 
 /* ---- decode workspace ----------------------------------------------------
  * Bytes of workspace one decode call over `batch` requests needs. Layout
- * (fp32, offsets from the workspace start, which must be 256-byte aligned):
- *   o_part  at 0:               [batch, n_q_heads, max_splits, head_dim]
+ * (offsets from the workspace start, which must be 256-byte aligned):
+ *   o_part  fp32 at 0:         [batch, n_q_heads, max_splits, head_dim]
  *           o_part[b,h,s,:] is split s's output, normalised by its own l
- *   ml_part at round_up(batch*n_q_heads*max_splits*head_dim*4, 256):
+ *   ml_part fp32 at round_up(batch*n_q_heads*max_splits*head_dim*4, 256):
  *           [batch, n_q_heads, max_splits, 2] = (m, l) with
  *           l = sum_{j in split} exp(x_j - m), x_j = scale * q.k_j; m is a
  *           finite stabiliser the kernel picks (one of the x_j seen so far), so
  *           only m + ln(l), the split's log-sum-exp, is uniquely defined.
- * Entries for s >= S_b are not written. Returns 0 if an argument is not positive
- * or max_splits > PKV_MAX_SPLITS. A workspace sized for batch B serves any batch <= B. */
+ * Entries for s >= S_b are not written; after pkv_paged_decode_attn or
+ * pkv_decode_step, requests with a single split may not have partials either
+ * (their output is written directly). Returns 0 if an argument is not positive
+ * or max_splits > PKV_MAX_SPLITS. A workspace sized for batch B serves any
+ * batch <= B with the same n_q_heads, head_dim and max_splits. */
 size_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head_dim,
                                   int32_t max_splits);
 
@@ -183,24 +186,45 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head
  *   out[b, h, :] = softmax_j(scale * q[b,h,:] . K[j]) V[j],  j < L_b,
  * with K[j], V[j] read at slot req_to_token[r_b, j] of `layer`. Computed as
  * split partials in the workspace (a3) followed by a log-sum-exp merge (a4);
- * rows with L_b = 0 produce zeros. q, out: device [batch, n_q_heads, head_dim]
- * of the pool dtype, 16-byte aligned; out is rounded to nearest-even.
- * The result is bit-identical run to run and does not depend on where the
- * slots sit in the pool. */
+ * a request with a single split is finished by the first kernel, the merge
+ * launch combines the others. Rows with L_b = 0 produce zeros.
+ * q, out: device [batch, n_q_heads, head_dim] of the pool dtype, 16-byte
+ * aligned; out is rounded to nearest-even. For BF16 the P.V products use P
+ * rounded to bf16 and the row sums use the same rounded values. The result is
+ * bit-identical run to run and does not depend on where the slots sit in the
+ * pool. Calls that share a workspace must not overlap in time. */
 pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                  int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
                                  pkv_split_cfg split, void* workspace, size_t ws_bytes,
                                  void* out, hipStream_t stream);
 
-/* a3 alone: writes the split partials of pkv_paged_decode_attn into the workspace. */
+/* a1 + a2 + a3 in one launch, then the a4 merge: the index step (each output only if its
+ * pointer is non-NULL: kv_indptr_out [batch+1], loc_out [batch], splits_out
+ * [batch], as pkv_build_metadata in DECODE mode), the store of each request's
+ * new token (k_new, v_new: device [batch, n_kv_heads, head_dim] of the pool
+ * dtype, 16-byte aligned, stored at slot req_to_token[r_b, L_b-1] as
+ * pkv_kv_store would with those locations; both NULL to skip the store) and
+ * the attention of pkv_paged_decode_attn, which reads the stored rows. The new
+ * tokens' slots must not be read by another request of the same call. */
+pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                           const void* k_new, const void* v_new, int32_t n_q_heads,
+                           const pkv_batch_meta* meta, float scale, pkv_split_cfg split,
+                           int32_t* kv_indptr_out, int32_t* loc_out, int32_t* splits_out,
+                           void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+
+/* a3 alone: writes the split partials of pkv_paged_decode_attn into the workspace
+ * (no merge, counters untouched). */
 pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
                                pkv_split_cfg split, void* workspace, size_t ws_bytes,
                                hipStream_t stream);
 
 /* a4 alone: merges the partials a pkv_decode_partials call with the same meta,
- * n_q_heads, head_dim and split left in the workspace:
- *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s exp(m_s - max_s' m_s'). */
+ * n_q_heads, head_dim and split left in the workspace (or partials a caller
+ * wrote there in the documented layout):
+ *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s exp(m_s - max_s' m_s').
+ * A request with one split gets that split's o unchanged (rounded to the output
+ * dtype), as pkv_paged_decode_attn does. */
 pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32_t head_dim,
                             int32_t dtype, pkv_split_cfg split, const void* workspace,
                             size_t ws_bytes, void* out, hipStream_t stream);

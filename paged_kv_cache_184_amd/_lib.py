@@ -27,7 +27,8 @@ PKV_MAX_SPLITS = 4096
 # Every symbol include/pkv.h declares.
 EXPORTS = (
     "pkv_abi_version", "pkv_status_str", "pkv_last_error", "pkv_kv_store", "pkv_build_metadata",
-    "pkv_decode_workspace_bytes", "pkv_paged_decode_attn", "pkv_decode_partials",
+    "pkv_decode_workspace_bytes", "pkv_paged_decode_attn",
+    "pkv_decode_step", "pkv_decode_partials",
     "pkv_decode_merge", "pkv_paged_prefill_attn", "pkv_validate_meta",
 )
 
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
         "pkv_kv_store": (I32, [pool_p, I32, P, P, P, I64, P]),
         "pkv_build_metadata": (I32, [meta_p, I32, SplitCfg, P, P, I64, P, P]),
         "pkv_decode_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "pkv_decode_step": (I32, [pool_p, I32, P, P, P, I32, meta_p, F32, SplitCfg, P, P, P, P, SZ,
+                                  P, P]),
         "pkv_paged_decode_attn": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P, P]),
         "pkv_decode_partials": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P]),
         "pkv_decode_merge": (I32, [meta_p, I32, I32, I32, SplitCfg, P, SZ, P, P]),

@@ -89,6 +89,7 @@ pkv_status check_split(pkv_split_cfg s) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// o_part at 0, ml_part at the next 256-byte boundary.
 size_t ws_bytes_for(int64_t batch, int64_t hq, int64_t d, int64_t max_splits, size_t* ml_off) {
   const size_t o = (size_t)(batch * hq * max_splits * d) * 4;
   const size_t ml = (size_t)(batch * hq * max_splits * 2) * 4;
@@ -106,6 +107,18 @@ pkv_status check_heads(const pkv_kv_pool* pool, int32_t n_q_heads) {
     return fail(PKV_EUNSUPPORTED, "group size %d not in {1, 2, 4, 8, 16}", g);
   if (pool->n_kv_heads > 65535) return fail(PKV_EUNSUPPORTED, "n_kv_heads > 65535");
   return PKV_OK;
+}
+
+char* a_k_layer(const pkv_kv_pool* pool, int32_t layer) {
+  const int64_t layer_bytes = pool->n_slots * pool->n_kv_heads * pool->head_dim *
+                              (int64_t)elem_bytes(pool->dtype);
+  return (char*)pool->k + (int64_t)layer * layer_bytes;
+}
+
+char* a_v_layer(const pkv_kv_pool* pool, int32_t layer) {
+  const int64_t layer_bytes = pool->n_slots * pool->n_kv_heads * pool->head_dim *
+                              (int64_t)elem_bytes(pool->dtype);
+  return (char*)pool->v + (int64_t)layer * layer_bytes;
 }
 
 pkv_status decode_prepare(const pkv_kv_pool* pool, int32_t layer, const void* q, int32_t n_q_heads,
@@ -129,10 +142,6 @@ pkv_status decode_prepare(const pkv_kv_pool* pool, int32_t layer, const void* q,
     if (ws_bytes < need)
       return fail(PKV_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
   }
-  const int64_t layer_elems = pool->n_slots * pool->n_kv_heads * pool->head_dim;
-  const int es = elem_bytes(pool->dtype);
-  a->k = (const char*)pool->k + (int64_t)layer * layer_elems * es;
-  a->v = (const char*)pool->v + (int64_t)layer * layer_elems * es;
   a->n_slots = pool->n_slots;
   a->n_kv_heads = pool->n_kv_heads;
   a->head_dim = pool->head_dim;
@@ -150,6 +159,14 @@ pkv_status decode_prepare(const pkv_kv_pool* pool, int32_t layer, const void* q,
   a->o_part = (float*)workspace;
   a->ml_part = workspace ? (float*)((char*)workspace + ml_off) : nullptr;
   a->out = nullptr;
+  a->merge_multi_only = false;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  a->k = (void*)a_k_layer(pool, layer);
+  a->v = (void*)a_v_layer(pool, layer);
+  a->kv_indptr_out = nullptr;
+  a->loc_out = nullptr;
+  a->splits_out = nullptr;
   return PKV_OK;
 }
 
@@ -278,8 +295,39 @@ pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const v
   if (!out) return fail(PKV_EINVAL, "out is NULL");
   if (!aligned16(out)) return fail(PKV_EALIGN, "out must be 16-byte aligned");
   a.out = out;
+  a.merge_multi_only = true;
   hipError_t e = pkv::launch_decode_partials(a, stream);
   if (e != hipSuccess) return hip_status(e, "decode partial launch");
+  return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
+}
+
+pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                           const void* k_new, const void* v_new, int32_t n_q_heads,
+                           const pkv_batch_meta* meta, float scale, pkv_split_cfg split,
+                           int32_t* kv_indptr_out, int32_t* loc_out, int32_t* splits_out,
+                           void* workspace, size_t ws_bytes, void* out, hipStream_t stream) {
+  pkv::DecodeArgs a;
+  pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
+  if (s != PKV_OK) return s;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(PKV_EINVAL, "k_new and v_new must both be set or both be NULL");
+  if (meta->batch == 0) {
+    if (kv_indptr_out) return hip_status(pkv::launch_zero(kv_indptr_out, 4, stream), "zero launch");
+    return ok();
+  }
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  if (!aligned16(out)) return fail(PKV_EALIGN, "out must be 16-byte aligned");
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+    return fail(PKV_EALIGN, "k_new / v_new must be 16-byte aligned");
+  a.out = out;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.kv_indptr_out = kv_indptr_out;
+  a.loc_out = loc_out;
+  a.splits_out = splits_out;
+  a.merge_multi_only = true;
+  hipError_t e = pkv::launch_decode_partials(a, stream);
+  if (e != hipSuccess) return hip_status(e, "decode step launch");
   return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
 }
 

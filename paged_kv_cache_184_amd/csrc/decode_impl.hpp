@@ -146,19 +146,43 @@ __device__ __forceinline__ void compute_tile(State<T, D, G>& st, const TileBuf<T
       st.m[h] = mnew;
     }
   }
-  float v0[E], v1[E];
+  if constexpr (sizeof(T) == 2) {
+    // P.V on v_dot2_f32_bf16: P is rounded to bf16 (hardware round-to-nearest-
+    // even) and the row sum takes the same rounded values; V needs no
+    // conversion, only pairing of the two tokens' values of each element.
+    uint32_t vp[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    v0[e] = elem<T, D>(buf.v[0], e);
-    v1[e] = elem<T, D>(buf.v[1], e);
-  }
+    for (int k = 0; k < Geo<T, D>::CH; ++k)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
-    const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
-    st.l[h] += p0 + p1;
+      for (int w = 0; w < 4; ++w) {
+        vp[k * 8 + 2 * w] = __builtin_amdgcn_perm(buf.v[1][k][w], buf.v[0][k][w], 0x05040100u);
+        vp[k * 8 + 2 * w + 1] = __builtin_amdgcn_perm(buf.v[1][k][w], buf.v[0][k][w], 0x07060302u);
+      }
 #pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(p1, v1[e], fmaf(p0, v0[e], st.acc[h][e]));
+    for (int h = 0; h < G; ++h) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
+      const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
+      const bf16x2_t pb = {(__bf16)p0, (__bf16)p1};
+      const uint32_t pp = __builtin_bit_cast(uint32_t, pb);
+      st.l[h] += bf16lo_to_f32(pp) + bf16hi_to_f32(pp);
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] = dot2_bf16(pp, vp[e], st.acc[h][e]);
+    }
+  } else {
+    float v0[E], v1[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      v0[e] = elem<T, D>(buf.v[0], e);
+      v1[e] = elem<T, D>(buf.v[1], e);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
+      const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
+      st.l[h] += p0 + p1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(p1, v1[e], fmaf(p0, v0[e], st.acc[h][e]));
+    }
   }
 }
 
@@ -214,9 +238,93 @@ __device__ __forceinline__ void super_tile(State<T, D, G>& st, const int* slots,
   }
 }
 
+// Log-sum-exp merge of the S partials of one (request, q head) for output
+// element d: out = sum_s w_s o_s / sum_s w_s, w_s = l_s exp(m_s - M), M the
+// largest m_s.
+__device__ __forceinline__ float merge_element(const float* __restrict__ ml,
+                                               const float* __restrict__ o, int S, int D, int d,
+                                               float M) {
+  constexpr int U = 8;
+  float acc = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < S; s0 += U) {
+    float ov[U], mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, S - 1);
+      mv[u] = ml[2 * s];
+      lv[u] = s0 + u < S ? ml[2 * s + 1] : 0.f;
+      ov[u] = o[(int64_t)s * D + d];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = lv[u] * __builtin_amdgcn_exp2f((mv[u] - M) * kLog2e);
+      den += w;
+      acc = fmaf(w, ov[u], acc);
+    }
+  }
+  return S > 0 ? acc * (1.0f / den) : 0.f;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
+  if constexpr (sizeof(T) == 2) {
+    ((__bf16*)out)[idx] = (__bf16)x;
+  } else {
+    ((float*)out)[idx] = x;
+  }
+}
+
+// Index step (a1) for the whole batch, run by one workgroup of 64*kWaves
+// threads: kv_indptr (exclusive prefix sum of seq_lens), new-token locations
+// and split counts; each output only if its pointer is set.
+__device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * kWaves;
+  const int B = a.batch;
+  const int per = (B + NT - 1) / NT;
+  const int begin = min(B, tid * per);
+  const int end = min(B, begin + per);
+  int local = 0;
+  for (int b = begin; b < end; ++b) local += a.seq_lens[b];
+  scan_lds[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < NT; off <<= 1) {
+    const int x = tid >= off ? scan_lds[tid - off] : 0;
+    __syncthreads();
+    scan_lds[tid] += x;
+    __syncthreads();
+  }
+  int run = scan_lds[tid] - local;
+  if (a.kv_indptr_out && tid == 0) a.kv_indptr_out[0] = 0;
+  for (int b = begin; b < end; ++b) {
+    int L = a.seq_lens[b];
+    run += L;
+    if (a.kv_indptr_out) a.kv_indptr_out[b + 1] = run;
+    L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+    if (a.loc_out)
+      a.loc_out[b] = L == 0 ? -1
+                            : a.req_to_token[(int64_t)clamp_index(a.req_pool_indices[b], a.n_rows) *
+                                                 a.stride + (L - 1)];
+    if (a.splits_out) {
+      int chunk;
+      a.splits_out[b] = split_count(L, a.split.max_splits, a.split.fixed_splits,
+                                    a.split.split_tokens, &chunk);
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per (request b, KV head, split s). Optional fused steps:
+//   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
+//     index step for the whole batch;
+//   a.k_new / v_new: the wave whose share holds position L-1 first stores the
+//     new token's K/V row of this KV head at slot req_to_token[r_b, L-1]
+//     (skipped if that slot is out of range), then reads it like any other;
+//   a.out: requests with one split are finished here (their normalised output
+//     is the result) and padded requests get zero rows; requests with more
+//     splits leave partials for the merge kernel.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * kWaves)
-void decode_partial_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
   using Gm = Geo<T, D>;
   constexpr int CH = Gm::CH;
   constexpr int E = Gm::E;
@@ -233,12 +341,22 @@ void decode_partial_kernel(DecodeArgs a) {
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
 
+  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
+    index_step_block(a, &slot_lds[0][0]);
+
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
   int chunk;
   const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
                             &chunk);
-  if (s >= S) return;
+  const int qh0 = kvh * G;
+  if (s >= S) {
+    // a padded request (L = 0) has no split: its rows are zero
+    if (S == 0 && s == 0 && a.out)
+      for (int i = tid; i < G * D; i += 64 * kWaves)
+        store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0) * D + i, 0.f);
+    return;
+  }
   const int lo = s * chunk;
   const int hi = min(L, lo + chunk);
   // this wave's contiguous share of the split, a multiple of 16 tokens
@@ -250,6 +368,24 @@ void decode_partial_kernel(DecodeArgs a) {
   const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
   const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
   const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
+
+  // fused store of the new token (position L-1) by the wave that reads it
+  if (a.k_new && L - 1 >= wlo && L - 1 < whi) {
+    const int raw = row[L - 1];
+    constexpr int CPR = Gm::ROW / 16;  // 16-byte chunks of one (slot, KV head) row
+    if (raw >= 0 && raw < n_slots && lane < 2 * CPR) {
+      const int chk = lane % CPR;
+      const char* src = (const char*)(lane < CPR ? a.k_new : a.v_new) +
+                        ((int64_t)b * a.n_kv_heads + kvh) * Gm::ROW + 16 * chk;
+      char* dst = (char*)(lane < CPR ? a.k : a.v) + (int64_t)raw * row_stride +
+                  (int64_t)kvh * Gm::ROW + 16 * chk;
+      *(u32x4*)dst = *(const u32x4*)src;
+    }
+    // the row is read back below by this same wave: complete the stores first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW + 16 * c;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW + 16 * c;
 
@@ -262,7 +398,7 @@ void decode_partial_kernel(DecodeArgs a) {
 
   // q chunks of the g heads, in the same lane layout as K.
   u32x4 q[G][CH];
-  const char* qbase = (const char*)a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G) * Gm::ROW + 16 * c;
+  const char* qbase = (const char*)a.q + ((int64_t)b * a.n_q_heads + qh0) * Gm::ROW + 16 * c;
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -329,9 +465,10 @@ void decode_partial_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the waves (fixed order) and write the split's partial.
-  const int qh0 = kvh * G;
-  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits + s;
+  // Merge the waves (fixed order). A request with a single split is finished
+  // here when an output is given; otherwise the split's partial is written.
+  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits;
+  const bool direct = a.out != nullptr && S == 1;
   for (int i = tid; i < G * D; i += 64 * kWaves) {
     const int h = i / D;
     const int d = i % D;
@@ -346,8 +483,13 @@ void decode_partial_kernel(DecodeArgs a) {
       num = fmaf(f, red_acc[w][h][d], num);
       den = fmaf(f, red_ml[w][h][1], den);
     }
-    const int64_t part = part0 + (int64_t)h * a.split.max_splits;
-    a.o_part[part * D + d] = num / den;
+    const float o = num / den;
+    if (direct) {
+      store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0 + h) * D + d, o);
+      continue;
+    }
+    const int64_t part = part0 + (int64_t)h * a.split.max_splits + s;
+    a.o_part[part * D + d] = o;
     if (d == 0) {
       float2 ml;
       ml.x = M * kLn2;
@@ -357,12 +499,11 @@ void decode_partial_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (request, q head): out = sum_s w_s o_s / sum_s w_s, reading
-// the partials eight splits at a time so their loads overlap.
+// One wave per (request, q head): the stand-alone merge (same arithmetic as the
+// fused one).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;  // elements per lane
-  constexpr int U = 8;
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -371,46 +512,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   int chunk;
   const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
                             &chunk);
+  // After the partial kernel ran with an output, requests with 0 or 1 split are
+  // already written.
+  if (a.merge_multi_only && S <= 1) return;
   const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
   const float* ml = a.ml_part + 2 * part;
-  const float* o = a.o_part + part * D + lane * PER;
-
-  // stabiliser: max of m over the splits, one split per lane, then across the wave
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
-  float acc[PER];
+  for (int t = 0; t < S; ++t) M = fmaxf(M, ml[2 * t]);
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  float den = 0.f;
-  for (int s0 = 0; s0 < S; s0 += U) {
-    float ov[U][PER], mv[U], lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = min(s0 + u, S - 1);
-      mv[u] = ml[2 * s];
-      lv[u] = s0 + u < S ? ml[2 * s + 1] : 0.f;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) ov[u][e] = o[(int64_t)s * D + e];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float w = lv[u] * __builtin_amdgcn_exp2f((mv[u] - M) * kLog2e);
-      den += w;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, ov[u][e], acc[e]);
-    }
-  }
-  const float inv = S > 0 ? 1.0f / den : 0.f;
-  const int64_t orow = ((int64_t)b * a.n_q_heads + h) * D + lane * PER;
-  if constexpr (sizeof(T) == 2) {
-    uint16_t* out = (uint16_t*)a.out + orow;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = (uint16_t)f32_to_bf16_rne(acc[e] * inv);
-  } else {
-    float* out = (float*)a.out + orow;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) out[e] = acc[e] * inv;
+  for (int e = 0; e < PER; ++e) {
+    const int d = lane * PER + e;
+    // one split: its normalised output is the result
+    const float x = S == 1 ? a.o_part[part * D + d] : merge_element(ml, a.o_part + part * D, S, D, d, M);
+    store_out<T>(a.out, ((int64_t)b * a.n_q_heads + h) * D + d, x);
   }
 }
 

@@ -10,8 +10,6 @@
 namespace pkv {
 
 struct DecodeArgs {
-  const void* k;  // layer base of the K pool (already offset by layer)
-  const void* v;
   int64_t n_slots;
   int32_t n_kv_heads;
   int32_t head_dim;
@@ -28,10 +26,20 @@ struct DecodeArgs {
   pkv_split_cfg split;
   float* o_part;
   float* ml_part;
-  void* out;
+  void* out;  // non-null: the partial kernel finishes requests with S <= 1 itself
+  bool merge_multi_only;  // merge kernel: leave requests with S <= 1 alone
+  // optional fused steps (all may be null)
+  const void* k_new;  // [batch, n_kv_heads, head_dim]: store at req_to_token[r_b, L_b-1]
+  const void* v_new;
+  void* k;  // pool layer bases, writable (for the fused store)
+  void* v;
+  int32_t* kv_indptr_out;
+  int32_t* loc_out;
+  int32_t* splits_out;
 };
 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
 hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,

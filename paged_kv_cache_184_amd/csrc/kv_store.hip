@@ -33,7 +33,26 @@ __global__ __launch_bounds__(256) void kv_store_kernel(char* __restrict__ k, cha
   *(u32x4*)(v + dst) = b;
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p16, uint8_t* __restrict__ tail,
+                                                   int64_t n16, int64_t ntail) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p16[i] = u32x4{0u, 0u, 0u, 0u};
+  if (i < ntail) tail[i] = 0;
+}
+
 }  // namespace
+
+// Zero a device buffer with a kernel (not a memset, so it can sit in a graph).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t ntail = (int64_t)(bytes % 16);
+  const int64_t work = n16 > ntail ? n16 : ntail;
+  const int64_t blocks = (work + 255) / 256;
+  zero_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>((u32x4*)p, (uint8_t*)p + n16 * 16, n16,
+                                                          ntail);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
                            const void* k_new, const void* v_new, const int32_t* loc,

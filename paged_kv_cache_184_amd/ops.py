@@ -131,8 +131,8 @@ def decode_workspace_bytes(batch: int, n_q_heads: int, head_dim: int, max_splits
 
 def alloc_decode_workspace(batch: int, n_q_heads: int, head_dim: int, max_splits: int,
                            device="cuda") -> torch.Tensor:
-    """A byte tensor big enough for pkv_decode_workspace_bytes (plain tensor even
-    under an inference-mode caller, so later in-place use from other threads works)."""
+    """A byte tensor of pkv_decode_workspace_bytes (a plain tensor even under an
+    inference-mode caller, so later in-place use from other threads works)."""
     n = decode_workspace_bytes(batch, n_q_heads, head_dim, max_splits)
     _need(n > 0, "invalid workspace arguments")
     with torch.inference_mode(False):
@@ -167,6 +167,32 @@ def paged_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: flo
     _check(lib().pkv_paged_decode_attn(C.byref(pool), layer, q.data_ptr(), q.shape[1],
                                        C.byref(meta), scale, split, workspace.data_ptr(),
                                        workspace.numel(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def decode_step(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float, split: SplitCfg,
+                workspace: torch.Tensor, k_new=None, v_new=None, kv_indptr_out=None, loc_out=None,
+                splits_out=None, out=None, stream=None):
+    """Index step + store of the new tokens + decode attention in one launch
+    (pkv_decode_step). k_new, v_new: [B, Hkv, D] or None."""
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    if k_new is not None:
+        _need(k_new.is_contiguous() and v_new is not None and v_new.is_contiguous(), "k_new/v_new")
+        _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "k_new/v_new dtype")
+        _need(k_new.numel() == meta.batch * pool.n_kv_heads * pool.head_dim, "k_new shape")
+        _need(v_new.numel() == k_new.numel(), "v_new shape")
+    for name, t, n in (("kv_indptr_out", kv_indptr_out, meta.batch + 1),
+                       ("loc_out", loc_out, meta.batch), ("splits_out", splits_out, meta.batch)):
+        if t is not None:
+            _need(t.dtype == torch.int32 and t.is_contiguous() and t.numel() >= n, name)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype, "out")
+    _check(lib().pkv_decode_step(C.byref(pool), layer, q.data_ptr(), _ptr(k_new), _ptr(v_new),
+                                 q.shape[1], C.byref(meta), scale, split, _ptr(kv_indptr_out),
+                                 _ptr(loc_out), _ptr(splits_out), workspace.data_ptr(),
+                                 workspace.numel(), out.data_ptr(), _stream(stream)))
     return out
 
 
@@ -244,6 +270,18 @@ def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, work
                             split, workspace.data_ptr(), workspace.numel(), out.data_ptr(), s,
                             keep=(pool, meta), stream=stream)
     raise ValueError(stage)
+
+
+def prepare_decode_step(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, workspace, out,
+                        k_new=None, v_new=None, kv_indptr_out=None, loc_out=None,
+                        splits_out=None, stream=None):
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    return PreparedCall("pkv_decode_step", C.byref(pool), layer, q.data_ptr(), _ptr(k_new),
+                        _ptr(v_new), q.shape[1], C.byref(meta), scale, split,
+                        _ptr(kv_indptr_out), _ptr(loc_out), _ptr(splits_out),
+                        workspace.data_ptr(), workspace.numel(), out.data_ptr(), None,
+                        keep=(pool, meta), stream=stream)
 
 
 def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None):

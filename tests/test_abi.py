@@ -193,6 +193,24 @@ def test_prefill_rejects(lib):
     assert f(C.byref(p), 0, 16, 4, C.byref(m), 0, 0, 0.1, 1, 16, None) == E.PKV_OK  # empty
 
 
+def test_decode_step_rejects(lib):
+    E = _lib
+    p = _pool()
+    m = _meta()
+    s = _split()
+    f = lib.pkv_decode_step
+    # only one of k_new / v_new
+    assert f(C.byref(p), 0, 16, 32, None, 4, C.byref(m), 0.1, s, None, None, None, 256, 1 << 20,
+             16, None) == E.PKV_EINVAL
+    # misaligned k_new
+    assert f(C.byref(p), 0, 16, 24, 32, 4, C.byref(m), 0.1, s, None, None, None, 256, 1 << 20,
+             16, None) == E.PKV_EALIGN
+    assert f(C.byref(p), 0, 16, 32, 48, 4, C.byref(m), 0.1, s, None, None, None, 256, 1 << 20,
+             None, None) == E.PKV_EINVAL
+    assert f(C.byref(p), 0, 16, 32, 48, 4, C.byref(m), 0.1, s, None, None, None, 256, 64,
+             16, None) == E.PKV_EWORKSPACE
+
+
 def test_validate_meta_rejects(lib):
     assert lib.pkv_validate_meta(C.byref(_meta()), 3, 10, 0, None) == _lib.PKV_EINVAL
     assert lib.pkv_validate_meta(None, 0, 10, 0, None) == _lib.PKV_EINVAL

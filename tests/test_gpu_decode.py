@@ -253,3 +253,96 @@ def test_error_leaves_output_untouched():
     assert e.value.name == "PKV_EWORKSPACE"
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+def test_decode_step_fused_matches_separate_calls():
+    """pkv_decode_step (index step + store + attention in one launch) against the
+    separate calls: index outputs and the stored pool bit-exact, output identical."""
+    b = W.ragged_decode(8)
+    vals = W.host_values(b, 140)
+    split = split_for(b, tokens=256)
+    # separate calls
+    db1 = DeviceBatch(b, vals)
+    loc1 = store_new_tokens(db1, 0)
+    ref_out, _ = run_decode(db1, 0, split)
+    # one fused launch
+    db2 = DeviceBatch(b, vals)
+    B = b.batch
+    ind = torch.full((B + 1,), -9, dtype=torch.int32, device=DEV)
+    loc = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    spl = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    ws = ops.alloc_decode_workspace(B, b.n_q_heads, b.head_dim, split.max_splits)
+    out = ops.decode_step(db2.q, db2.k_pool, db2.v_pool, 0, db2.meta(), b.scale, split, ws,
+                          k_new=db2.k_new, v_new=db2.v_new, kv_indptr_out=ind, loc_out=loc,
+                          splits_out=spl)
+    torch.cuda.synchronize()
+    assert np.array_equal(ind.cpu().numpy(), O.kv_indptr(b.seq_lens))
+    assert np.array_equal(loc.cpu().numpy(), loc1.cpu().numpy())
+    S, _ = O.split_plan(b.seq_lens, split.max_splits, split.fixed_splits, split.split_tokens)
+    assert np.array_equal(spl.cpu().numpy(), S)
+    assert torch.equal(db2.k_pool.view(torch.int16), db1.k_pool.view(torch.int16))
+    assert torch.equal(db2.v_pool.view(torch.int16), db1.v_pool.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    ref, _, _ = oracle_after_store(b, vals, 0)
+    compare(out.float().cpu().numpy(), ref, "bf16", "fused decode step")
+
+
+def test_repeated_calls_and_shrinking_batch():
+    """Repeated calls on one workspace, with the batch changing, stay exact."""
+    b = W.custom("rep", n_layers=1, n_slots=1 << 16, n_q_heads=32, n_kv_heads=8, head_dim=128,
+                 dtype="bf16", seq_lens=[5000, 3000, 1, 800, 4096, 2222], n_new=[1] * 6, seed=150)
+    vals = W.host_values(b, 151)
+    db = DeviceBatch(b, vals)
+    split = ops.split_cfg(64, 0, 128)
+    ws = ops.alloc_decode_workspace(6, 32, 128, 64)
+    ref = O.decode_attention(vals.q, vals.k_pool, vals.v_pool, 0, b.req_to_token,
+                             b.req_pool_indices, b.seq_lens, b.scale)
+    first = None
+    for it in range(5):
+        out = ops.paged_decode_attn(db.q, db.k_pool, db.v_pool, 0, db.meta(), b.scale, split, ws)
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+            compare(out.float().cpu().numpy(), ref, "bf16", "repeated call 0")
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16)), it
+    # a smaller batch (first 3 requests) on the same workspace
+    meta3 = ops.make_meta(db.r2t, db.rows[:3].contiguous(), db.lens[:3].contiguous())
+    out3 = ops.paged_decode_attn(db.q[:3].contiguous(), db.k_pool, db.v_pool, 0, meta3, b.scale,
+                                 split, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out3.view(torch.int16), first[:3].view(torch.int16))
+    # and the full batch again
+    out = ops.paged_decode_attn(db.q, db.k_pool, db.v_pool, 0, db.meta(), b.scale, split, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), first.view(torch.int16))
+
+
+def test_decode_step_under_graph_replay():
+    """A captured decode step replays bit-exactly, with eager work and syncs
+    between replays (the library records no memset and no allocation)."""
+    b = W.ragged_decode(8)
+    vals = W.host_values(b, 160)
+    db = DeviceBatch(b, vals)
+    split = split_for(b, tokens=256)
+    ws = ops.alloc_decode_workspace(b.batch, b.n_q_heads, b.head_dim, split.max_splits)
+    out = torch.empty_like(db.q)
+    call = ops.prepare_decode_step(db.q, db.k_pool, db.v_pool, 0, db.meta(), b.scale, split, ws,
+                                   out, k_new=db.k_new, v_new=db.v_new)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        _ = (db.q.float() * 2).sum().item()  # unrelated eager work between replays
