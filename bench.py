@@ -40,7 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--ctx", type=int, nargs="*", default=[1024, 4096, 16384, 32768])
     p.add_argument("--headline", type=int, default=32768)
-    p.add_argument("--split-tokens", type=int, default=256)
+    p.add_argument("--split-tokens", type=int, default=0,
+                   help="tokens per split; 0 = ops.choose_split for the workload")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -65,6 +66,8 @@ def profile_run(args):
     db = DecodeBench(args.headline, n_layers=8, split_tokens=args.split_tokens, seed=184_002)
     for i in range(max(8, args.steps)):
         db.step(i)
+    torch.cuda.synchronize()
+    db.run_partials(max(8, args.steps), 2)
     torch.cuda.synchronize()
     print(json.dumps({"profile": "done", "copy_bytes": n, "steps": max(8, args.steps),
                       "partial_kernel_bytes": db.partial_kernel_bytes()}), flush=True)
@@ -123,8 +126,11 @@ class DecodeBench:
         self.rows = torch.from_numpy(b.req_pool_indices).to(dev)
         self.lens = torch.from_numpy(b.seq_lens).to(dev)
         self.meta = ops.make_meta(self.r2t, self.rows, self.lens)
-        max_splits = max(1, -(-ctx // split_tokens))
-        self.split = ops.split_cfg(max_splits, 0, split_tokens)
+        if split_tokens > 0:
+            self.split = ops.split_cfg(max(1, -(-ctx // split_tokens)), 0, split_tokens)
+        else:
+            self.split = ops.choose_split(ctx, b.batch, b.n_kv_heads)
+        max_splits = self.split.max_splits
         self.ws = ops.alloc_decode_workspace(B, b.n_q_heads, b.head_dim, max_splits)
         self.out = torch.empty_like(self.q)
         self.kv_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
@@ -214,6 +220,33 @@ class DecodeBench:
         step_ms = start.elapsed_time(end) / steps
         part_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         return step_ms, part_ms, host_s
+
+    def run_partials(self, steps: int, warmup: int):
+        """Average duration of the split-partial kernel alone (HIP events around
+        each launch, on the launch stream), same configuration as the step."""
+        torch = self.torch
+        parts = [self.ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta,
+                                         self.b.scale, self.split, self.ws, self.out,
+                                         stage="partials")
+                 for layer in range(self.b.n_layers)]
+        for i in range(warmup):
+            parts[i % len(parts)]()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))]
+        t = time.perf_counter()
+        for i in range(4):
+            parts[i % len(parts)]()
+        enqueue_s = (time.perf_counter() - t) / 4
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(min(2e9, max(1e5, 3.0 * steps * enqueue_s * spin_cycles_per_s()))))
+        # back-to-back launches between two events: the per-launch average
+        # carries no event overhead, only the (sub-microsecond) launch gaps
+        evs[0][0].record()
+        for i in range(steps):
+            parts[i % len(parts)]()
+        evs[0][1].record()
+        torch.cuda.synchronize()
+        return evs[0][0].elapsed_time(evs[0][1]) / steps
 
     def run_graph(self, steps: int):
         torch = self.torch
@@ -354,6 +387,31 @@ class PrefillBench:
         return step_ms, attn_ms
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_b1_32k_traffic.json")
+KERNEL_SOURCES = ["paged_kv_cache_184_amd/csrc/decode_impl.hpp",
+                  "paged_kv_cache_184_amd/csrc/decode_bf16_d128.hip",
+                  "paged_kv_cache_184_amd/csrc/common.hpp"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the partial kernel from the committed counter
+    runs, or None when the kernel sources changed since they were taken."""
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for rel in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] != rec["source_hash"]:
+            return None
+        return round(float(rec["traffic_bytes"]) / 1e6, 2)
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(db: DecodeBench, seconds: float):
     """Time the fp64 oracle on the headline workload until ``seconds`` of CPU
     work have run; report KV GB/s in the same unit as the GPU."""
@@ -398,17 +456,18 @@ def main():
         db.mode = "separate"
         sep_ms, sep_attn_ms, _ = db.run(args.steps, args.warmup)
         db.mode = "fused"
-        step_ms, part_ms, host_s = db.run(args.steps, args.warmup)
+        step_ms, call_ms, host_s = db.run(args.steps, args.warmup)
+        part_ms = db.run_partials(args.steps, args.warmup)
         err = db.check()
         entry = {
             "us_per_step": round(step_ms * 1e3, 2),
             "kv_gbs": round(db.kv_bytes() / (step_ms * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100 * db.step_bytes() / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-            "kernel_us": round(part_ms * 1e3, 2),
-            "kernel_gbs": round(db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9, 1),
+            "partial_kernel_us": round(part_ms * 1e3, 2),
+            "partial_kernel_gbs": round(db.partial_kernel_bytes() / (part_ms * 1e-3) / 1e9, 1),
             "separate_calls_us_per_step": round(sep_ms * 1e3, 2),
-            "separate_attn_kernel_us": round(sep_attn_ms * 1e3, 2),
             "splits": int(db.split.max_splits),
+            "split_tokens": int(db.split.split_tokens),
             "max_abs_err": err,
         }
         if args.graph:
@@ -455,13 +514,16 @@ def main():
         "config": {"workload": f"b1_decode_{args.headline // 1024}k", "batch": 1,
                    "context": args.headline, "n_q_heads": 32, "n_kv_heads": 8, "head_dim": 128,
                    "kv_dtype": "bf16", "pool_slots": 40960, "layers_rotated": 8,
-                   "slot_layout": "shuffled 16-token pages", "split_tokens": args.split_tokens},
+                   "slot_layout": "shuffled 16-token pages",
+                   "split_tokens": int(db.split.split_tokens)},
         "pct_hbm_peak": detail[f"{args.headline // 1024}k"]["pct_hbm_peak"],
         "us_per_step": round(step_ms * 1e3, 2),
         "host_s_timed_region": round(host_s, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_partial_kernel<bf16,128,4> (fused decode step)"},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(), "traffic_unit": "MB per launch",
+                     "algorithmic_bytes_per_launch": db.partial_kernel_bytes(),
+                     "kernel": "decode_partial_kernel<bf16,128,4>"},
         "detail": detail,
     }
     if not args.no_cpu:
