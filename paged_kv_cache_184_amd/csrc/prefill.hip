@@ -12,9 +12,13 @@
 // share a KV head share every K/V tile (BQ = 128 / g tokens per tile).
 //
 // Per 64-key block:
-//   * the 256 threads gather the block's K rows (16-byte loads through the
-//     slot table) into LDS row-major, and its V rows into LDS transposed
-//     ([d][key], two keys packed per dword), both with padded row strides;
+//   * K and V rows are gathered through the slot table straight into LDS
+//     (global_load_lds_dwordx4, no registers), row-major with the 16-byte
+//     chunks of row r XOR-swizzled by r, into a ring of kStages stages: the
+//     block two ahead is in flight while one is computed. Each wave waits for
+//     its own transfers with an explicit vmcnt; one barrier per block then
+//     publishes the stage and frees the oldest one. Slot ids arrive the same
+//     way one block ahead, so the queue is never drained inside the loop.
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand for the whole tile);
@@ -23,8 +27,11 @@
 //     sums accumulate those rounded values;
 //   * O^T += V^T P^T with the same MFMA: P^T comes straight out of the S^T
 //     accumulator layout (lane l holds keys 4(l/16)+r of two 16-key tiles for
-//     query column l%16), V^T is read from the transposed LDS tile with the
-//     same key order, so no register shuffles are needed.
+//     query column l%16); V^T comes from the row-major V tile through
+//     ds_read_b64_tr_b16, which hands lane i of each 16-lane group element
+//     i%4 of the 8-byte segments of lanes i/4, i/4+4, i/4+8, i/4+12: pointing
+//     those lanes at keys base+4g+0..3 and columns 16dt+4(s%4) gives every
+//     lane the 4 keys it needs at its own column.
 // Only blocks that straddle the causal diagonal or the sequence end are
 // masked. Tiles are issued longest-first (highest token offset first).
 #include <math.h>
@@ -38,37 +45,56 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kBK = 64;      // keys per block
 constexpr int kThreads = 256;
+constexpr int kStages = 3;
 constexpr float kTau = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct PGeo {
-  static constexpr int ROW = D * 2;          // bytes of a (slot, KV head) row
-  static constexpr int KS = ROW + 16;        // LDS row stride of the K tile
-  static constexpr int VS = kBK * 2 + 8;     // LDS row stride of the V^T tile
-  static constexpr int K_BYTES = kBK * KS;
-  static constexpr int V_BYTES = D * VS;
-  static constexpr int KSTEPS = D / 32;      // MFMA k-steps over head_dim
-  static constexpr int DT = D / 16;          // 16-wide output tiles over head_dim
-  static constexpr int CPR = ROW / 16;       // 16-byte chunks per row
+  static constexpr int ROW = D * 2;              // bytes of a (slot, KV head) row
+  static constexpr int CPR = ROW / 16;           // 16-byte chunks per row (8 or 16)
+  static constexpr int RPI = 64 / CPR;           // rows per wave-wide 1 KiB transfer
+  static constexpr int NI = (kBK / 4) / RPI;     // transfers per wave per tile (K or V)
+  static constexpr int TILE = kBK * ROW;         // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int KSTEPS = D / 32;          // MFMA k-steps over head_dim
+  static constexpr int DT = D / 16;              // 16-wide output tiles over head_dim
 };
+
+// vmcnt(n) alone (expcnt, lgkmcnt left at their maxima), gfx9 encoding
+#define PKV_VMCNT(n) ((((n) & 15)) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+
+#define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define PKV_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t bf16_round(float x) { return f32_to_bf16_rne(x); }
+// Byte offset of logical 16-byte chunk c of row r in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * PGeo<D>::ROW + 16 * (c ^ (r & (PGeo<D>::CPR - 1)));
+}
+
+template <int D>
+__device__ __forceinline__ u32x2 tr_read(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <int D, int G, bool MASK>
 __device__ __forceinline__ void attend_block(
-    const char* __restrict__ lds_k, const char* __restrict__ lds_v, const u32x4 (&qf)[2][PGeo<D>::KSTEPS],
-    f32x4 (&o)[PGeo<D>::DT][2], float (&m)[2], float (&l)[2], int k0, const int (&limit)[2],
-    float scale2, int lane) {
+    const char* __restrict__ lds_k, const char* __restrict__ lds_v,
+    const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], float (&m)[2],
+    float (&l)[2], int k0, const int (&limit)[2], float scale2, int lane) {
   using Gm = PGeo<D>;
   const int col = lane & 15;
   const int quad = lane >> 4;
@@ -80,7 +106,7 @@ __device__ __forceinline__ void attend_block(
     s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < Gm::KSTEPS; ++ks) {
-      const u32x4 a = *(const u32x4*)(lds_k + (16 * kt + col) * Gm::KS + 2 * (32 * ks + 8 * quad));
+      const u32x4 a = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
       s[kt][0] = mfma16(a, qf[0][ks], s[kt][0]);
       s[kt][1] = mfma16(a, qf[1][ks], s[kt][1]);
     }
@@ -135,24 +161,29 @@ __device__ __forceinline__ void attend_block(
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const uint32_t lo = bf16_round(__builtin_amdgcn_exp2f(s[2 * j + h][n][r] - mm));
-          const uint32_t hi = bf16_round(__builtin_amdgcn_exp2f(s[2 * j + h][n][r + 1] - mm));
-          lsum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
-          w[2 * h + r / 2] = lo | (hi << 16);
+          const bf16x2_t pb = {(__bf16)__builtin_amdgcn_exp2f(s[2 * j + h][n][r] - mm),
+                               (__bf16)__builtin_amdgcn_exp2f(s[2 * j + h][n][r + 1] - mm)};
+          const uint32_t pp = __builtin_bit_cast(uint32_t, pb);
+          lsum += bf16lo_to_f32(pp) + bf16hi_to_f32(pp);
+          w[2 * h + r / 2] = pp;
         }
       }
       pf[n][j] = u32x4{w[0], w[1], w[2], w[3]};
     }
     l[n] += lsum;
   }
-  // O^T += V^T P^T
+  // O^T += V^T P^T; V^T fragments by transpose reads of the row-major V tile.
+  const int s4 = col & 3;
 #pragma unroll
   for (int dt = 0; dt < Gm::DT; ++dt) {
+    // column 16dt + 4(s%4) lives in logical chunk 2dt + (s%4)/2, half (s%2)
+    const int chunk = 2 * dt + (s4 >> 1);
+    const int half = 8 * (s4 & 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const char* vrow = lds_v + (16 * dt + col) * Gm::VS + 2 * (32 * j + 4 * quad);
-      const u32x2 lo = *(const u32x2*)(vrow);
-      const u32x2 hi = *(const u32x2*)(vrow + 32);  // keys +16
+      const int r0 = 32 * j + 4 * quad + (col >> 2);
+      const u32x2 lo = tr_read<D>(lds_v + swz<D>(r0, chunk) + half);
+      const u32x2 hi = tr_read<D>(lds_v + swz<D>(r0 + 16, chunk) + half);
       const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
       o[dt][0] = mfma16(a, pf[0][j], o[dt][0]);
       o[dt][1] = mfma16(a, pf[1][j], o[dt][1]);
@@ -164,9 +195,16 @@ template <int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   using Gm = PGeo<D>;
   constexpr int BQ = kRows / G;  // tokens per tile
-  __shared__ __attribute__((aligned(16))) char lds[Gm::K_BYTES + Gm::V_BYTES];
-  char* lds_k = lds;
-  char* lds_v = lds + Gm::K_BYTES;
+  // One LDS object per ring stage (tiles and slot ids), selected with
+  // compile-time indices, so reads of one stage are not ordered behind the
+  // transfers into another.
+  __shared__ __attribute__((aligned(1024))) char st0[Gm::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Gm::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[Gm::STAGE];
+  __shared__ __attribute__((aligned(16))) int id0[4][kBK];  // [wave][row]
+  __shared__ __attribute__((aligned(16))) int id1[4][kBK];
+  __shared__ __attribute__((aligned(16))) int id2[4][kBK];
+  static_assert(kStages == 3, "three ring stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,13 +225,54 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int t_last = min(t0 + BQ, n_new) - 1;
   const int kv_end = a.causal ? P + t_last + 1 : L;  // keys the tile can see
   const int kv_full = a.causal ? P + t0 + 1 : L;     // keys every row of the tile sees
+  const int nblk = (kv_end + kBK - 1) / kBK;
 
   const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
   const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
   const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
   const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
+
+  // This lane's transfer rows and logical chunk: transfer i of this wave
+  // covers tile rows 16*wave + RPI*i .. +RPI-1; lane l lands at physical chunk
+  // l % CPR of row 16*wave + RPI*i + l / CPR, so it fetches the logical chunk
+  // that the swizzle puts there.
+  const int prow = lane / Gm::CPR;
+  const int pch = lane % Gm::CPR;
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
+
+  // Slot ids of a block arrive by DMA too (one 4-byte transfer per lane into a
+  // per-wave ring in LDS), so every vector-memory operation of the loop is
+  // under the explicit wait counts below. Positions past the end are clamped.
+  auto id_ring = [&](int ring) -> int* {
+    return ring == 0 ? &id0[wave][0] : (ring == 1 ? &id1[wave][0] : &id2[wave][0]);
+  };
+  auto stage_ptr = [&](int ring) -> char* { return ring == 0 ? st0 : (ring == 1 ? st1 : st2); };
+  auto load_ids = [&](int blk, int ring) {
+    const int kb = min(blk, nblk - 1) * kBK;
+    const int32_t* src = row + min(kb + lane, kv_end - 1);
+    __builtin_amdgcn_global_load_lds(PKV_GLB(src), PKV_LDS(id_ring(ring)), 4, 0, 0);
+  };
+  auto offsets = [&](int ring, int64_t (&off)[Gm::NI]) {
+    const int* ids = id_ring(ring);
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      const int rr = 16 * wave + Gm::RPI * i + prow;
+      const int lch = pch ^ (rr & (Gm::CPR - 1));
+      off[i] = (int64_t)clamp_index(ids[rr], n_slots) * row_stride + 16 * lch;
+    }
+  };
+  auto issue = [&](int stage, const int64_t (&off)[Gm::NI]) {
+    char* st = stage_ptr(stage);
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      const int rbase = 16 * wave + Gm::RPI * i;
+      __builtin_amdgcn_global_load_lds(PKV_GLB(kbase + off[i]), PKV_LDS(st + rbase * Gm::ROW), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(PKV_GLB(vbase + off[i]),
+                                       PKV_LDS(st + Gm::TILE + rbase * Gm::ROW), 16, 0, 0);
+    }
+  };
 
   // Q^T fragments (B operand) for this wave's two 16-row tiles.
   const int col = lane & 15;
@@ -224,47 +303,46 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   float lsum[2] = {0.f, 0.f};
   const float scale2 = a.scale * kLog2e;
 
-  for (int k0 = 0; k0 < kv_end; k0 += kBK) {
-    __syncthreads();  // previous block's LDS reads are done
-    // K: 64 keys x CPR chunks, row-major, coalesced 16-byte loads.
+  // Transfer order per wave, kept identical in every iteration so that the
+  // explicit wait counts are exact: before block i is computed the queue holds,
+  // oldest first, D(i) S(i+2) D(i+1) S(i+3), where D(k) = 2*NI tile transfers
+  // of block k and S(k) = one slot-id transfer for block k. Block indices past
+  // the end are clamped, so the counts never change.
+  int64_t off[Gm::NI];
+  load_ids(0, 0);
+  load_ids(1, 1);
+  __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  offsets(0, off);
+  issue(0, off);
+  load_ids(2, 2);
+  offsets(1, off);
+  issue(1, off);
+
+  constexpr int kAfter = 2 * Gm::NI + 1;  // D(i+1) S(i+3) may still be in flight
+  for (int i0 = 0; i0 < nblk; i0 += kStages) {
 #pragma unroll
-    for (int i = 0; i < (kBK * Gm::CPR) / kThreads; ++i) {
-      const int c = tid + kThreads * i;
-      const int j = c / Gm::CPR;
-      const int cc = c % Gm::CPR;
-      const int pos = min(k0 + j, kv_end - 1);
-      const int slot = clamp_index(row[pos], n_slots);
-      const u32x4 x = *(const u32x4*)(kbase + (int64_t)slot * row_stride + 16 * cc);
-      *(u32x4*)(lds_k + j * Gm::KS + 16 * cc) = x;
+    for (int u = 0; u < kStages; ++u) {
+      const int i = i0 + u;
+      if (i >= nblk) break;
+      // ring stage of block k is k % 3: block i+3 reuses stage u, block i+2 is (u+2) % 3
+      load_ids(i + 3, u);
+      __builtin_amdgcn_s_waitcnt(PKV_VMCNT(kAfter));  // D(i) and S(i+2) landed (this wave)
+      __builtin_amdgcn_s_barrier();                     // ... for every wave; stage i-1 is free
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      offsets((u + 2) % kStages, off);
+      issue((u + 2) % kStages, off);
+      const char* st = stage_ptr(u);
+      const int k0 = i * kBK;
+      if (k0 + kBK <= kv_full && k0 + kBK <= L)
+        attend_block<D, G, false>(st, st + Gm::TILE, qf, o, m, lsum, k0, limit, scale2, lane);
+      else
+        attend_block<D, G, true>(st, st + Gm::TILE, qf, o, m, lsum, k0, limit, scale2, lane);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
-    // V: each thread takes two adjacent keys of one chunk and writes them
-    // transposed, two keys per dword.
-#pragma unroll
-    for (int i = 0; i < (kBK / 2 * Gm::CPR) / kThreads; ++i) {
-      const int c = tid + kThreads * i;
-      const int j2 = c % (kBK / 2);
-      const int cc = c / (kBK / 2);
-      const int pa = min(k0 + 2 * j2, kv_end - 1);
-      const int pb = min(k0 + 2 * j2 + 1, kv_end - 1);
-      const int sa = clamp_index(row[pa], n_slots);
-      const int sb = clamp_index(row[pb], n_slots);
-      const u32x4 va = *(const u32x4*)(vbase + (int64_t)sa * row_stride + 16 * cc);
-      const u32x4 vb = *(const u32x4*)(vbase + (int64_t)sb * row_stride + 16 * cc);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8cc + 2w (low halves) and 8cc + 2w + 1 (high halves)
-        const uint32_t lo = (va[w] & 0xffffu) | (vb[w] << 16);
-        const uint32_t hi = (va[w] >> 16) | (vb[w] & 0xffff0000u);
-        *(uint32_t*)(lds_v + (8 * cc + 2 * w) * Gm::VS + 4 * j2) = lo;
-        *(uint32_t*)(lds_v + (8 * cc + 2 * w + 1) * Gm::VS + 4 * j2) = hi;
-      }
-    }
-    __syncthreads();
-    if (k0 + kBK <= kv_full && k0 + kBK <= L)
-      attend_block<D, G, false>(lds_k, lds_v, qf, o, m, lsum, k0, limit, scale2, lane);
-    else
-      attend_block<D, G, true>(lds_k, lds_v, qf, o, m, lsum, k0, limit, scale2, lane);
   }
+  // drain the transfers still in flight before the workgroup exits
+  __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
 
   // Row sums: the four lanes of a query column hold disjoint keys.
 #pragma unroll
@@ -284,9 +362,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt) {
       const int d = 16 * dt + 4 * quad;
+      const bf16x2_t w0 = {(__bf16)(o[dt][n][0] * inv), (__bf16)(o[dt][n][1] * inv)};
+      const bf16x2_t w1 = {(__bf16)(o[dt][n][2] * inv), (__bf16)(o[dt][n][3] * inv)};
       u32x2 w;
-      w[0] = pack_bf16x2(o[dt][n][0] * inv, o[dt][n][1] * inv);
-      w[1] = pack_bf16x2(o[dt][n][2] * inv, o[dt][n][3] * inv);
+      w[0] = __builtin_bit_cast(uint32_t, w0);
+      w[1] = __builtin_bit_cast(uint32_t, w1);
       *(u32x2*)(out + d) = w;
     }
   }
