@@ -171,31 +171,19 @@ class DecodeBench:
         return (self.partial_kernel_bytes() + b.batch * b.n_q_heads * b.head_dim * 2 +
                 2 * 2 * b.batch * b.n_kv_heads * b.head_dim * 2)
 
-    def step(self, i: int, ev=None):
-        """One decode step for layer i mod n_layers; ev brackets the attention kernel."""
+    def step(self, i: int):
+        """One decode step for layer i mod n_layers."""
         if self.mode == "fused":
-            if ev is not None:
-                ev[0].record()
             self.fused[i % len(self.fused)]()
-            if ev is not None:
-                ev[1].record()
             return
-        meta_call, store_call, attn_call = self.calls[i % len(self.calls)]
-        meta_call()
-        store_call()
-        if ev is not None:
-            ev[0].record()
-        attn_call()
-        if ev is not None:
-            ev[1].record()
+        for call in self.calls[i % len(self.calls)]:
+            call()
 
     def run(self, steps: int, warmup: int):
         torch = self.torch
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         # host time to enqueue one step, and the device spin rate, so the hold
@@ -211,15 +199,15 @@ class DecodeBench:
         # hold the stream so the host enqueues the K steps ahead of the GPU; the
         # start event is recorded after the hold
         torch.cuda._sleep(cycles)
+        # only two events, around all K steps: an event between steps would put
+        # a marker between the kernels and lengthen the step
         start.record()
         for i in range(steps):
-            self.step(i, evs[i])
+            self.step(i)
         end.record()
         torch.cuda.synchronize()
         host_s = time.perf_counter() - t0
-        step_ms = start.elapsed_time(end) / steps
-        part_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        return step_ms, part_ms, host_s
+        return start.elapsed_time(end) / steps, host_s
 
     def run_partials(self, steps: int, warmup: int):
         """Average duration of the split-partial kernel alone (HIP events around
@@ -390,7 +378,8 @@ class PrefillBench:
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_b1_32k_traffic.json")
 KERNEL_SOURCES = ["paged_kv_cache_184_amd/csrc/decode_impl.hpp",
                   "paged_kv_cache_184_amd/csrc/decode_bf16_d128.hip",
-                  "paged_kv_cache_184_amd/csrc/common.hpp"]
+                  "paged_kv_cache_184_amd/csrc/common.hpp",
+                  "paged_kv_cache_184_amd/csrc/internal.hpp"]
 
 
 def measured_traffic():
@@ -407,7 +396,7 @@ def measured_traffic():
                 h.update(f.read())
         if h.hexdigest()[:16] != rec["source_hash"]:
             return None
-        return round(float(rec["traffic_bytes"]) / 1e6, 2)
+        return int(round(float(rec["traffic_bytes"])))
     except (OSError, KeyError, ValueError):
         return None
 
@@ -454,9 +443,9 @@ def main():
     for ctx in args.ctx:
         db = DecodeBench(ctx, n_layers=8, split_tokens=args.split_tokens, seed=184_002 + ctx)
         db.mode = "separate"
-        sep_ms, sep_attn_ms, _ = db.run(args.steps, args.warmup)
+        sep_ms, _ = db.run(args.steps, args.warmup)
         db.mode = "fused"
-        step_ms, call_ms, host_s = db.run(args.steps, args.warmup)
+        step_ms, host_s = db.run(args.steps, args.warmup)
         part_ms = db.run_partials(args.steps, args.warmup)
         err = db.check()
         entry = {
@@ -521,7 +510,7 @@ def main():
         "host_s_timed_region": round(host_s, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "traffic_unit": "MB per launch",
+                     "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
                      "algorithmic_bytes_per_launch": db.partial_kernel_bytes(),
                      "kernel": "decode_partial_kernel<bf16,128,4>"},
         "detail": detail,

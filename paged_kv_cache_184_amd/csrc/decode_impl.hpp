@@ -9,7 +9,8 @@
 // (same page, bullet on removing Storage.gather); int32 indices (same page).
 //
 // Partial kernel: one workgroup of kWaves waves per (request b, KV head, split
-// s); each wave takes a contiguous quarter of the split's tokens.
+// s); each wave takes a contiguous share (a multiple of 16 tokens) of the
+// split's tokens.
 //   * Lanes form 8 groups of 8; group t handles tokens t and t+8 of a 16-token
 //     tile, lane c of the group holds 16-byte chunks c, c+8, ... of the
 //     token's K and V rows (D*es bytes per (slot, KV head)), so every load is a
@@ -186,7 +187,7 @@ __device__ __forceinline__ void compute_tile(State<T, D, G>& st, const TileBuf<T
   }
 }
 
-constexpr int kWaves = 4;   // waves per workgroup; each takes a quarter of the split
+constexpr int kWaves = 4;  // waves per workgroup, each taking a contiguous share of the split
 constexpr int kTiles = 8;   // 16-token tiles per super-tile (straight-line, fully unrolled)
 constexpr int kSuper = 16 * kTiles;
 
@@ -238,33 +239,6 @@ __device__ __forceinline__ void super_tile(State<T, D, G>& st, const int* slots,
   }
 }
 
-// Log-sum-exp merge of the S partials of one (request, q head) for output
-// element d: out = sum_s w_s o_s / sum_s w_s, w_s = l_s exp(m_s - M), M the
-// largest m_s.
-__device__ __forceinline__ float merge_element(const float* __restrict__ ml,
-                                               const float* __restrict__ o, int S, int D, int d,
-                                               float M) {
-  constexpr int U = 8;
-  float acc = 0.f, den = 0.f;
-  for (int s0 = 0; s0 < S; s0 += U) {
-    float ov[U], mv[U], lv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = min(s0 + u, S - 1);
-      mv[u] = ml[2 * s];
-      lv[u] = s0 + u < S ? ml[2 * s + 1] : 0.f;
-      ov[u] = o[(int64_t)s * D + d];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float w = lv[u] * __builtin_amdgcn_exp2f((mv[u] - M) * kLog2e);
-      den += w;
-      acc = fmaf(w, ov[u], acc);
-    }
-  }
-  return S > 0 ? acc * (1.0f / den) : 0.f;
-}
-
 template <typename T>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   if constexpr (sizeof(T) == 2) {
@@ -274,12 +248,11 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float x) {
   }
 }
 
-// Index step (a1) for the whole batch, run by one workgroup of 64*kWaves
-// threads: kv_indptr (exclusive prefix sum of seq_lens), new-token locations
+// Index step (a1) for the whole batch, run by one workgroup of NT threads: kv_indptr (exclusive prefix sum of seq_lens), new-token locations
 // and split counts; each output only if its pointer is set.
+template <int NT>
 __device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
   const int tid = threadIdx.x;
-  constexpr int NT = 64 * kWaves;
   const int B = a.batch;
   const int per = (B + NT - 1) / NT;
   const int begin = min(B, tid * per);
@@ -342,7 +315,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int b = blockIdx.z;
 
   if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
-    index_step_block(a, &slot_lds[0][0]);
+    index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
 
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
@@ -499,11 +472,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   }
 }
 
-// One wave per (request, q head): the stand-alone merge (same arithmetic as the
-// fused one).
+// One wave per (request, q head). Splits are taken 32 at a time: all 32
+// partial rows and (m, l) pairs of a group are loaded before anything waits
+// (one memory round trip for up to 32 splits), the group's weights
+// w_s = l_s exp(m_s - M) are computed one split per lane and shared through
+// LDS, and the running stabiliser M is raised between groups (acc and the
+// weight sum rescaled), so the result is sum_s w_s o_s / sum_s w_s.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;  // elements per lane
+  constexpr int U = 32;        // splits per group
+  __shared__ float wts[U];
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -516,16 +495,51 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   // already written.
   if (a.merge_multi_only && S <= 1) return;
   const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
-  const float* ml = a.ml_part + 2 * part;
-  float M = -INFINITY;
-  for (int t = 0; t < S; ++t) M = fmaxf(M, ml[2 * t]);
+  const float2* ml = (const float2*)(a.ml_part + 2 * part);
+  const float* o = a.o_part + part * D + lane * PER;
+  const int64_t orow = ((int64_t)b * a.n_q_heads + h) * D + lane * PER;
+  if (S <= 1) {  // no split: zeros; one split: its normalised output is the result
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int d = lane * PER + e;
-    // one split: its normalised output is the result
-    const float x = S == 1 ? a.o_part[part * D + d] : merge_element(ml, a.o_part + part * D, S, D, d, M);
-    store_out<T>(a.out, ((int64_t)b * a.n_q_heads + h) * D + d, x);
+    for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, S == 1 ? o[e] : 0.f);
+    return;
   }
+  float M = -INFINITY, den = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < S; c0 += U) {
+    const int n = min(U, S - c0);
+    float ov[U][PER];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[u][e] = o[(int64_t)(c0 + min(u, n - 1)) * D + e];
+    float2 mlv = make_float2(-INFINITY, 0.f);
+    if (lane < n) mlv = ml[c0 + lane];
+    const float Mn = fmaxf(M, wave_max(mlv.x));  // finite: the group is not empty
+    const float r = __builtin_amdgcn_exp2f((M - Mn) * kLog2e);  // 0 on the first group
+    M = Mn;
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] *= r;
+    const float w = lane < n ? mlv.y * __builtin_amdgcn_exp2f((mlv.x - M) * kLog2e) : 0.f;
+    den += w;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // earlier reads of wts first
+    if (lane < U) wts[lane] = w;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = wts[u];  // 0 past the group's end
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(wu, ov[u][e], acc[e]);
+    }
+  }
+  // sum of the weights over the wave (butterfly: every lane gets the same bits)
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off);
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, acc[e] * inv);
 }
 
 template <typename T, int D>
