@@ -28,8 +28,8 @@
  *   Query head h of a request reads KV head h / (n_q_heads / n_kv_heads).
  *
  * Supported: dtype F32 or BF16 (Q, K, V and output share it; accumulation is
- * always fp32), head_dim 64 or 128, group size n_q_heads / n_kv_heads in
- * {1, 2, 4, 8, 16}.
+ * always fp32; prefill is BF16 only), head_dim 64 or 128, group size
+ * n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}.
  *
  * Memory safety: kernels clamp every device-supplied index to the buffer it
  * addresses (slots to [0, n_slots), request rows to [0, n_req_rows), positions
@@ -213,7 +213,7 @@ pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q
                            void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* a3 alone: writes the split partials of pkv_paged_decode_attn into the workspace
- * (no merge, counters untouched). */
+ * (no merge). */
 pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
                                pkv_split_cfg split, void* workspace, size_t ws_bytes,
@@ -237,8 +237,11 @@ pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32
  * start into one forward; P1, bullet on cached prefix pages). The new tokens'
  * K/V must already be stored (pkv_kv_store). q, out: device
  * [total_q, n_q_heads, head_dim], 16-byte aligned. max_q_len >= every n_b sizes
- * the grid (rows i >= max_q_len are not computed). QK^T and PV run on bf16 MFMA
- * for BF16 (P is rounded to bf16 for PV; the row sums use those rounded values). */
+ * the grid (rows i >= max_q_len are not computed). BF16 pools only (any other
+ * dtype returns PKV_EUNSUPPORTED): QK^T and PV run on bf16 MFMA with fp32
+ * accumulation, P is rounded to bf16 for PV and the row sums use those rounded
+ * values; any finite scale, including 0 and negative values. Bit-identical run
+ * to run and independent of where the slots sit in the pool. */
 pkv_status pkv_paged_prefill_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                   int32_t n_q_heads, const pkv_batch_meta* meta,
                                   int32_t total_q, int32_t max_q_len, float scale,

@@ -14,17 +14,21 @@
 // Per 64-key block:
 //   * K and V rows are gathered through the slot table straight into LDS
 //     (global_load_lds_dwordx4, no registers), row-major with the 16-byte
-//     chunks of row r XOR-swizzled by r, into a ring of kStages stages: the
-//     block two ahead is in flight while one is computed. Each wave waits for
-//     its own transfers with an explicit vmcnt; one barrier per block then
-//     publishes the stage and frees the oldest one. Slot ids arrive the same
-//     way one block ahead, so the queue is never drained inside the loop.
+//     chunks of row r XOR-swizzled by r, into a two-stage ring: the next block
+//     is in flight while one is computed. Each wave waits for its own
+//     transfers with an explicit vmcnt; one barrier per block then publishes
+//     the stage and frees the other one. Slot ids arrive the same way two
+//     blocks ahead, so the queue is never drained inside the loop. The ring
+//     (66 KiB) and a 256-register cap let two workgroups share a CU, so one
+//     wave's softmax overlaps the other's MFMAs on each SIMD.
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand for the whole tile);
 //   * softmax in base 2 with a per-row stabiliser that is raised only when a
-//     score exceeds it by more than kTau; P is rounded to bf16 and the row
-//     sums accumulate those rounded values;
+//     score exceeds it by more than kTau (tested on the raw row maxima; the
+//     scale folds into the exponent's FMA); P is rounded to bf16 and the row
+//     sums are those rounded values summed by one more MFMA (a ones operand
+//     times P^T);
 //   * O^T += V^T P^T with the same MFMA: P^T comes straight out of the S^T
 //     accumulator layout (lane l holds keys 4(l/16)+r of two 16-key tiles for
 //     query column l%16); V^T comes from the row-major V tile through
@@ -50,8 +54,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kBK = 64;      // keys per block
 constexpr int kThreads = 256;
-constexpr int kStages = 3;
-constexpr float kTau = 8.0f;
+constexpr int kStages = 2;
+constexpr float kTau = 64.0f;  // log2 headroom of the fixed stabiliser
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -90,109 +94,126 @@ __device__ __forceinline__ u32x2 tr_read(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <int D, int G, bool MASK>
+// bf16 1.0 in both halves: the A operand whose product with P^T gives the
+// row sums of P (every output row of the tile is the same sum).
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+// One 64-key block for this wave's 32 query rows, taken as two 32-key halves
+// (S, stabiliser check, P and O for one half before the next) so that only one
+// half's scores are live. scale2 > 0 (the caller negates Q for a negative
+// scale and zeroes it for a zero scale), so the largest scaled score is the
+// scaled largest raw score, the scale folds into the exponent's FMA and a
+// masked score (-inf) gives weight 0.
+//
+// The stabiliser m of a row is fixed for the whole pass and O is never
+// rescaled here: m is set from the first 32 keys (init), and a later score
+// more than kTau above it only sets `bad` (the caller then recomputes the tile
+// with m = the exact row maxima, collected in mseen). With kTau = 64 the
+// weights stay below 2^64, so P, the row sums and O stay far from the fp32 /
+// bf16 range limit until `bad` is raised.
+template <int D, int G>
 __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
-    const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], float (&m)[2],
-    float (&l)[2], int k0, const int (&limit)[2], float scale2, int lane) {
+    const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
+    float (&m)[2], float (&mseen)[2], bool& bad, bool init, bool mask, int k0,
+    const int (&limit)[2], float scale2, int lane) {
   using Gm = PGeo<D>;
+  constexpr int KS = Gm::KSTEPS;
   const int col = lane & 15;
   const int quad = lane >> 4;
-  // S^T for 4 key tiles x 2 query tiles
-  f32x4 s[4][2];
+  const int s4 = col & 3;
+  const u32x4 ones = u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
-    s[kt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    s[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; ++j) {
+    // S^T for key tiles 2j, 2j+1 x 2 query tiles
+    f32x4 s[2][2];
 #pragma unroll
-    for (int ks = 0; ks < Gm::KSTEPS; ++ks) {
-      const u32x4 a = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
-      s[kt][0] = mfma16(a, qf[0][ks], s[kt][0]);
-      s[kt][1] = mfma16(a, qf[1][ks], s[kt][1]);
-    }
-  }
-  // scale, mask, stabiliser check
-  bool need = false;
+    for (int h = 0; h < 2; ++h) {
+      const int kt = 2 * j + h;
+      s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = s[kt][n][r] * scale2;
-        if (MASK) {
-          const int key = k0 + 16 * kt + 4 * quad + r;
-          x = key <= limit[n] ? x : -INFINITY;
-        }
-        s[kt][n][r] = x;
-        need |= x > m[n] + kTau;
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 ka = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
+        s[h][0] = mfma16(ka, qf[0][ks], s[h][0]);
+        s[h][1] = mfma16(ka, qf[1][ks], s[h][1]);
       }
     }
-  }
-  if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    // mask (blocks on the causal diagonal or the sequence end only), then the
+    // stabiliser check on the raw maxima
+    if (mask) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + 32 * j + 16 * h + 4 * quad + r;
+            s[h][n][r] = key <= limit[n] ? s[h][n][r] : -INFINITY;
+          }
+    }
+    float mx[2];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][n][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[n], mx);
-      // rows that have seen no visible key yet keep m = -inf (their p are 0)
-      const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[n] - mnew);
-      l[n] *= corr;
-#pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt) o[dt][n] *= corr;
-      m[n] = mnew;
+      const float x = fmaxf(fmaxf(fmaxf(s[0][n][0], s[0][n][1]), fmaxf(s[0][n][2], s[0][n][3])),
+                            fmaxf(fmaxf(s[1][n][0], s[1][n][1]), fmaxf(s[1][n][2], s[1][n][3])));
+      mx[n] = x * scale2;  // scale2 > 0: a fully masked lane keeps -inf
     }
-  }
-  // P^T (bf16) in the B-operand layout: slots 0..3 = key tile 2j, 4..7 = tile 2j+1
-  u32x4 pf[2][2];
+    if (init && j == 0) {
+      // first 32 keys of the tile's first pass: the stabiliser is their row
+      // maximum (key 0 is visible to every row, so it is finite); O and the
+      // row sums are still zero, so nothing is rescaled
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const float mm = m[n] == -INFINITY ? 0.f : m[n];
-    float lsum = 0.f;
+      for (int n = 0; n < 2; ++n) {
+        float x = fmaxf(mx[n], __shfl_xor(mx[n], 16));
+        m[n] = fmaxf(x, __shfl_xor(x, 32));
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int n = 0; n < 2; ++n) {
+      mseen[n] = fmaxf(mseen[n], mx[n]);
+      bad |= mx[n] > m[n] + kTau;
+    }
+    // P^T (bf16) in the B-operand layout: slots 0..3 = key tile 2j, 4..7 = tile 2j+1
+    u32x4 pf[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float nm = m[n] == -INFINITY ? 0.f : -m[n];
       uint32_t w[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int r = 0; r < 4; r += 2) {
-          const bf16x2_t pb = {(__bf16)__builtin_amdgcn_exp2f(s[2 * j + h][n][r] - mm),
-                               (__bf16)__builtin_amdgcn_exp2f(s[2 * j + h][n][r + 1] - mm)};
-          const uint32_t pp = __builtin_bit_cast(uint32_t, pb);
-          lsum += bf16lo_to_f32(pp) + bf16hi_to_f32(pp);
-          w[2 * h + r / 2] = pp;
+          // a masked key (-inf) gives exp2(-inf) = 0
+          const bf16x2_t pb = {
+              (__bf16)__builtin_amdgcn_exp2f(fmaf(s[h][n][r], scale2, nm)),
+              (__bf16)__builtin_amdgcn_exp2f(fmaf(s[h][n][r + 1], scale2, nm))};
+          w[2 * h + r / 2] = __builtin_bit_cast(uint32_t, pb);
         }
       }
-      pf[n][j] = u32x4{w[0], w[1], w[2], w[3]};
+      pf[n] = u32x4{w[0], w[1], w[2], w[3]};
     }
-    l[n] += lsum;
-  }
-  // O^T += V^T P^T; V^T fragments by transpose reads of the row-major V tile.
-  const int s4 = col & 3;
+    // row sums of the rounded P: ones x P^T
+    lacc[0] = mfma16(ones, pf[0], lacc[0]);
+    lacc[1] = mfma16(ones, pf[1], lacc[1]);
+    // O^T += V^T P^T; V^T fragments by transpose reads of the row-major V tile.
+    // Column 16dt + 4(s%4) lives in logical chunk 2dt + (s%4)/2, half (s%2).
+    const int r0 = 32 * j + 4 * quad + (col >> 2);
 #pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt) {
-    // column 16dt + 4(s%4) lives in logical chunk 2dt + (s%4)/2, half (s%2)
-    const int chunk = 2 * dt + (s4 >> 1);
-    const int half = 8 * (s4 & 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r0 = 32 * j + 4 * quad + (col >> 2);
+    for (int dt = 0; dt < Gm::DT; ++dt) {
+      const int chunk = 2 * dt + (s4 >> 1);
+      const int half = 8 * (s4 & 1);
       const u32x2 lo = tr_read<D>(lds_v + swz<D>(r0, chunk) + half);
       const u32x2 hi = tr_read<D>(lds_v + swz<D>(r0 + 16, chunk) + half);
-      const u32x4 a = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      o[dt][0] = mfma16(a, pf[0][j], o[dt][0]);
-      o[dt][1] = mfma16(a, pf[1][j], o[dt][1]);
+      const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      o[dt][0] = mfma16(va, pf[0], o[dt][0]);
+      o[dt][1] = mfma16(va, pf[1], o[dt][1]);
     }
   }
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Gm = PGeo<D>;
   constexpr int BQ = kRows / G;  // tokens per tile
   // One LDS object per ring stage (tiles and slot ids), selected with
@@ -200,11 +221,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   // transfers into another.
   __shared__ __attribute__((aligned(1024))) char st0[Gm::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[Gm::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[Gm::STAGE];
   __shared__ __attribute__((aligned(16))) int id0[4][kBK];  // [wave][row]
   __shared__ __attribute__((aligned(16))) int id1[4][kBK];
-  __shared__ __attribute__((aligned(16))) int id2[4][kBK];
-  static_assert(kStages == 3, "three ring stages");
+  __shared__ int redo[4];  // per wave: a score rose past the stabiliser's headroom
+  static_assert(kStages == 2, "two ring stages");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,10 +264,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   // Slot ids of a block arrive by DMA too (one 4-byte transfer per lane into a
   // per-wave ring in LDS), so every vector-memory operation of the loop is
   // under the explicit wait counts below. Positions past the end are clamped.
-  auto id_ring = [&](int ring) -> int* {
-    return ring == 0 ? &id0[wave][0] : (ring == 1 ? &id1[wave][0] : &id2[wave][0]);
-  };
-  auto stage_ptr = [&](int ring) -> char* { return ring == 0 ? st0 : (ring == 1 ? st1 : st2); };
+  auto id_ring = [&](int ring) -> int* { return ring == 0 ? &id0[wave][0] : &id1[wave][0]; };
+  auto stage_ptr = [&](int ring) -> char* { return ring == 0 ? st0 : st1; };
   auto load_ids = [&](int blk, int ring) {
     const int kb = min(blk, nblk - 1) * kBK;
     const int32_t* src = row + min(kb + lane, kv_end - 1);
@@ -293,63 +311,85 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     limit[n] = a.causal ? min(P + tc, L - 1) : L - 1;
   }
 
-  f32x4 o[Gm::DT][2];
+  // a negative scale is applied as -scale on -Q (bf16 negation is exact), a
+  // zero scale as scale 1 on Q = 0 (every score is exactly 0 either way)
+  float scale2 = a.scale * kLog2e;
+  if (!(scale2 > 0.f)) {
+    const uint32_t flip = scale2 < 0.f ? 0x80008000u : 0u;
+    const uint32_t keep = scale2 < 0.f ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt) {
-    o[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-    o[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int ks = 0; ks < Gm::KSTEPS; ++ks) qf[n][ks] = (qf[n][ks] & keep) ^ flip;
+    scale2 = scale2 < 0.f ? -scale2 : 1.f;
   }
+
+  f32x4 o[Gm::DT][2];
+  f32x4 lacc[2];
   float m[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  const float scale2 = a.scale * kLog2e;
-
-  // Transfer order per wave, kept identical in every iteration so that the
-  // explicit wait counts are exact: before block i is computed the queue holds,
-  // oldest first, D(i) S(i+2) D(i+1) S(i+3), where D(k) = 2*NI tile transfers
-  // of block k and S(k) = one slot-id transfer for block k. Block indices past
-  // the end are clamped, so the counts never change.
-  int64_t off[Gm::NI];
-  load_ids(0, 0);
-  load_ids(1, 1);
-  __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  offsets(0, off);
-  issue(0, off);
-  load_ids(2, 2);
-  offsets(1, off);
-  issue(1, off);
-
-  constexpr int kAfter = 2 * Gm::NI + 1;  // D(i+1) S(i+3) may still be in flight
-  for (int i0 = 0; i0 < nblk; i0 += kStages) {
+  float mseen[2] = {-INFINITY, -INFINITY};
+  bool bad = false;
+  // Pass 0 fixes each row's stabiliser from its first 32 keys. Pass 1 runs only
+  // if some score of the tile rose more than kTau above it; it starts from the
+  // exact row maxima that pass 0 saw, so it cannot overflow.
+  for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) {
-      const int i = i0 + u;
-      if (i >= nblk) break;
-      // ring stage of block k is k % 3: block i+3 reuses stage u, block i+2 is (u+2) % 3
-      load_ids(i + 3, u);
-      __builtin_amdgcn_s_waitcnt(PKV_VMCNT(kAfter));  // D(i) and S(i+2) landed (this wave)
-      __builtin_amdgcn_s_barrier();                     // ... for every wave; stage i-1 is free
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      offsets((u + 2) % kStages, off);
-      issue((u + 2) % kStages, off);
-      const char* st = stage_ptr(u);
-      const int k0 = i * kBK;
-      if (k0 + kBK <= kv_full && k0 + kBK <= L)
-        attend_block<D, G, false>(st, st + Gm::TILE, qf, o, m, lsum, k0, limit, scale2, lane);
-      else
-        attend_block<D, G, true>(st, st + Gm::TILE, qf, o, m, lsum, k0, limit, scale2, lane);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int dt = 0; dt < Gm::DT; ++dt) {
+      o[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    lacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool first_pass = pass == 0;
+
+    // Transfer order per wave, kept identical in every iteration so that the
+    // explicit wait counts are exact: before block i is computed the queue
+    // holds, oldest first, S(i+1) D(i) S(i+2), where D(k) = 2*NI tile transfers
+    // of block k into stage k % 2 and S(k) = one slot-id transfer for block k
+    // into id ring k % 2. Block indices past the end are clamped, so the counts
+    // never change.
+    int64_t off[Gm::NI];
+    load_ids(0, 0);
+    load_ids(1, 1);
+    __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    offsets(0, off);
+    issue(0, off);
+
+    for (int i0 = 0; i0 < nblk; i0 += kStages) {
+#pragma unroll
+      for (int u = 0; u < kStages; ++u) {
+        const int i = i0 + u;
+        if (i >= nblk) break;
+        load_ids(i + 2, u);  // ring u held the ids of block i, already consumed
+        __builtin_amdgcn_s_waitcnt(PKV_VMCNT(1));  // S(i+1) and D(i) landed (this wave)
+        __builtin_amdgcn_s_barrier();              // ... for every wave; block i-1 is done
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        offsets(u ^ 1, off);
+        issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
+        const char* st = stage_ptr(u);
+        const int k0 = i * kBK;
+        const bool init = first_pass && i == 0;
+        const bool mask = k0 + kBK > kv_full || k0 + kBK > L;
+        attend_block<D, G>(st, st + Gm::TILE, qf, o, lacc, m, mseen, bad, init, mask, k0, limit,
+                           scale2, lane);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      }
+    }
+    // drain the transfers still in flight (before a second pass or the exit)
+    __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
+    if (!first_pass) break;
+    // workgroup-wide decision; the barrier also frees the stages for pass 1
+    if (lane == 0) redo[wave] = __builtin_amdgcn_ballot_w64(bad) != 0;
+    __syncthreads();
+    if (!(redo[0] | redo[1] | redo[2] | redo[3])) break;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      float x = fmaxf(mseen[n], __shfl_xor(mseen[n], 16));
+      m[n] = fmaxf(x, __shfl_xor(x, 32));
     }
   }
-  // drain the transfers still in flight before the workgroup exits
-  __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
 
-  // Row sums: the four lanes of a query column hold disjoint keys.
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    lsum[n] += __shfl_xor(lsum[n], 16);
-    lsum[n] += __shfl_xor(lsum[n], 32);
-  }
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int rr = wave * 32 + n * 16 + col;
@@ -357,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int64_t orow = ((int64_t)q0 + tok[n]) * a.n_q_heads + (int64_t)kvh * G + rr % G;
     const int64_t t_abs = (int64_t)q0 + tok[n];
     if (t_abs < 0 || t_abs >= a.total_q) continue;
-    const float inv = 1.0f / lsum[n];
+    const float inv = 1.0f / lacc[n][0];  // the row sum over all keys, in every lane of the column
     uint16_t* out = (uint16_t*)a.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt) {

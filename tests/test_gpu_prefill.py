@@ -4,7 +4,8 @@ The new tokens' K/V go through the index step and kv_store first, as in the
 real step. Covers the packed-prefill workload (sampled rows at full size, all
 rows on a reduced copy), ragged tails around the 64-key block and the
 128-row tile, empty requests, every supported group size and head_dim, the
-non-causal variant, single-visible-key rows (exact), determinism, slot
+non-causal variant, zero and negative scales, scores that rise far past the
+first keys' maximum, single-visible-key rows (exact), determinism, slot
 relocation and decode/prefill agreement.
 """
 
@@ -62,6 +63,44 @@ def test_ragged_small(causal):
                  dtype="bf16", seq_lens=[1, 33, 64 + 31, 200, 63 + 65, 100, 7],
                  n_new=[1, 33, 31, 200, 65, 0, 7], seed=200)
     check_batch(b, 201, causal=causal)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883, 0.0625])
+def test_scale_zero_and_negative(scale):
+    # zero: every visible key weighs the same; negative: the ordering of scores flips
+    b = W.custom(f"scale{scale}", n_layers=1, n_slots=4096, n_q_heads=8, n_kv_heads=2,
+                 head_dim=128, dtype="bf16", seq_lens=[150, 70], n_new=[90, 70], seed=260,
+                 scale=scale)
+    check_batch(b, 261)
+
+
+def test_scores_rising_far_past_first_keys():
+    """q . k_j = j along each sequence (scale 1): later keys outscore the first
+    32 by far more than any fixed headroom, so every tile that sees them has to
+    be recomputed from its exact row maxima."""
+    b = W.custom("rising", n_layers=1, n_slots=4096, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                 dtype="bf16", seq_lens=[300, 129, 40], n_new=[200, 129, 40], seed=270, scale=1.0)
+    vals = W.host_values(b, 271)
+    q = np.zeros_like(vals.q)
+    q[:, :, 0] = 8.0
+    k_pool = vals.k_pool.copy()
+    k_new = vals.k_new.copy()
+    for i in range(b.batch):
+        L = int(b.seq_lens[i])
+        n = int(b.n_new[i])
+        P = L - n
+        row = b.req_to_token[b.req_pool_indices[i]]
+        for j in range(P):
+            k_pool[0, row[j], :, 0] = j / 8.0
+        lo = int(b.qo_indptr[i])
+        for t in range(n):
+            k_new[lo + t, :, 0] = (P + t) / 8.0
+    vals = W.Values(q, W.round_to_bf16(k_new), vals.v_new, W.round_to_bf16(k_pool), vals.v_pool)
+    db = DeviceBatch(b, vals)
+    store_prefill_tokens(db, 0)
+    out = run_prefill(db, 0)
+    ref = oracle_prefill(b, vals, 0)
+    compare(out.float().cpu().numpy(), ref, "bf16", "rising scores")
 
 
 @pytest.mark.parametrize("g,d", [(1, 128), (2, 64), (4, 64), (8, 128), (16, 128), (16, 64)])
