@@ -44,6 +44,7 @@ def parse():
                    help="tokens per split; 0 = ops.choose_split for the workload")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-batches", action="store_true", help="skip the batched decode workloads")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="also time HIP-graph replay")
     p.add_argument("--profile", action="store_true",
@@ -63,7 +64,10 @@ def profile_run(args):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    db = DecodeBench(args.headline, n_layers=8, split_tokens=args.split_tokens, seed=184_002)
+    from paged_kv_cache_184_amd import workloads as W
+
+    db = DecodeBench(W.b1_decode(args.headline, n_layers=8), split_tokens=args.split_tokens,
+                     seed=184_002)
     for i in range(max(8, args.steps)):
         db.step(i)
     torch.cuda.synchronize()
@@ -96,15 +100,16 @@ def spin_cycles_per_s() -> float:
 class DecodeBench:
     """Device state of one B=1 decode workload and its prepared library calls."""
 
-    def __init__(self, ctx: int, n_layers: int, split_tokens: int, seed: int):
+    def __init__(self, b, split_tokens: int, seed: int):
+        """b: a decode workload (one new token per request) with n_layers
+        identical layers to rotate over."""
         import torch
 
         from paged_kv_cache_184_amd import ops
-        from paged_kv_cache_184_amd import workloads as W
 
         self.torch, self.ops = torch, ops
-        b = W.b1_decode(ctx, n_layers=n_layers)
         self.b = b
+        ctx = int(b.seq_lens.max())
         dev = "cuda"
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
@@ -158,6 +163,9 @@ class DecodeBench:
     # algorithmic bytes
     def kv_bytes(self) -> int:
         return self.b.kv_bytes_logical()
+
+    def kv_bytes_unique(self) -> int:
+        return self.b.kv_bytes_unique()
 
     def partial_kernel_bytes(self) -> int:
         b = self.b
@@ -277,9 +285,9 @@ class DecodeBench:
         k = self.k_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
         v = self.v_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
         r2t = np.arange(L, dtype=np.int32)[None]
-        ref = O.decode_attention(self.q.float().cpu().numpy(), k, v, 0, r2t,
+        ref = O.decode_attention(self.q[:1].float().cpu().numpy(), k, v, 0, r2t,
                                  np.array([0], np.int32), np.array([L], np.int32), b.scale)
-        return float(np.abs(self.out.float().cpu().numpy() - ref).max())
+        return float(np.abs(self.out[:1].float().cpu().numpy() - ref).max())
 
     def oracle_inputs(self):
         b = self.b
@@ -288,7 +296,7 @@ class DecodeBench:
         idx = self.torch.from_numpy(slots.astype(np.int64)).to("cuda")
         k = self.k_pool[0].index_select(0, idx).float().cpu().numpy()[None]
         v = self.v_pool[0].index_select(0, idx).float().cpu().numpy()[None]
-        return (self.q.float().cpu().numpy(), k, v, np.arange(L, dtype=np.int32)[None],
+        return (self.q[:1].float().cpu().numpy(), k, v, np.arange(L, dtype=np.int32)[None],
                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
 
 
@@ -440,8 +448,11 @@ def main():
         return
     detail = {}
     head = None
+    from paged_kv_cache_184_amd import workloads as W
+
     for ctx in args.ctx:
-        db = DecodeBench(ctx, n_layers=8, split_tokens=args.split_tokens, seed=184_002 + ctx)
+        db = DecodeBench(W.b1_decode(ctx, n_layers=8), split_tokens=args.split_tokens,
+                         seed=184_002 + ctx)
         db.mode = "separate"
         sep_ms, _ = db.run(args.steps, args.warmup)
         db.mode = "fused"
@@ -468,6 +479,35 @@ def main():
         if ctx == args.headline:
             head = (db, step_ms, part_ms, host_s)
         else:
+            del db
+            torch.cuda.empty_cache()
+    if not args.no_batches:
+        # batched decode workloads: ragged B=8 / B=32 with a shared 2048-token
+        # prefix, and B=64 lognormal lengths over a fragmented 2^21-slot pool
+        # (plus the same lengths in 16-token pages, to separate the cost of the
+        # token-granular scatter from the kernel's)
+        for name, make in (("ragged_b8", lambda: W.ragged_decode(8, n_layers=8)),
+                           ("ragged_b32", lambda: W.ragged_decode(32, n_layers=8)),
+                           ("large_b64", lambda: W.large_batch_decode(n_layers=4)),
+                           ("large_b64_pages16",
+                            lambda: W.large_batch_decode(n_layers=4, layout="pages16"))):
+            db = DecodeBench(make(), split_tokens=0, seed=184_010 + len(name))
+            steps = max(10, args.steps // 4)
+            db.mode = "fused"
+            step_ms, _ = db.run(steps, max(2, args.warmup // 4))
+            err = db.check()
+            b = db.b
+            detail[name] = {
+                "batch": b.batch, "n_q_heads": b.n_q_heads, "sum_seq_lens": int(b.seq_lens.sum()),
+                "max_seq_len": int(b.seq_lens.max()), "us_per_step": round(step_ms * 1e3, 2),
+                "kv_gbs_logical": round(db.kv_bytes() / (step_ms * 1e-3) / 1e9, 1),
+                "kv_gbs_unique": round(db.kv_bytes_unique() / (step_ms * 1e-3) / 1e9, 1),
+                "pct_hbm_peak_unique": round(100 * (db.step_bytes() - db.kv_bytes() +
+                                                    db.kv_bytes_unique()) /
+                                             (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+                "splits": int(db.split.max_splits), "split_tokens": int(db.split.split_tokens),
+                "max_abs_err_request0": err}
+            print(f"# {name}: {detail[name]}", file=sys.stderr, flush=True)
             del db
             torch.cuda.empty_cache()
     if not args.no_prefill:

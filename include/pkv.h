@@ -146,6 +146,28 @@ pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_ne
                         const void* v_new, const int32_t* loc, int64_t n_tokens,
                         hipStream_t stream);
 
+/* ---- rotary embedding of the new tokens fused with their store ----------
+ * For every t < n_tokens, with p = positions[t] clamped to [0, max_pos):
+ *   q_out[t, h] = rope(q[t, h], p)             for h < n_q_heads (if q != NULL)
+ *   k[layer, loc[t]] = rope(k_new[t]);  v[layer, loc[t]] = v_new[t]
+ * (P1, bullet on extending the rotary embedding to packed 3D inputs; P4, bullet
+ * on the rotary table holding cos / sin values). rope rotates pair i of a row
+ * by the table entry freqs_cis[p, i] = (cos, sin): a' = a cos - b sin,
+ * b' = b cos + a sin, in fp32, rounded to the pool dtype (nearest-even for
+ * BF16). Pair i is (2i, 2i+1) when interleaved = 1, else (i, i + head_dim/2).
+ * Stores follow pkv_kv_store: loc outside [0, n_slots) is skipped, locations
+ * must be unique within one call, v is copied bit-exactly.
+ * q, q_out: device [n_tokens, n_q_heads, head_dim] of the pool dtype, 16-byte
+ * aligned; q_out may equal q (in place); both NULL to rotate only k.
+ * k_new, v_new: device [n_tokens, n_kv_heads, head_dim], 16-byte aligned, not
+ * modified. positions, loc: device int32 [n_tokens]. freqs_cis: device float
+ * [max_pos, head_dim/2, 2], 8-byte aligned. */
+pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* q, void* q_out,
+                             int32_t n_q_heads, const void* k_new, const void* v_new,
+                             const int32_t* positions, const float* freqs_cis, int32_t max_pos,
+                             int32_t interleaved, const int32_t* loc, int64_t n_tokens,
+                             hipStream_t stream);
+
 /* ---- a1: index step ----------------------------------------------------
  * Writes, each only if its pointer is non-NULL (P1, bullet on updating
  * position_ids / seq_lens / kv_indptr in place each decode step):

@@ -30,4 +30,7 @@ from .paged_attention import (  # noqa: F401
     lse_merge,
     prefill_attention,
     gathered_kv,
+    rope_pairs,
+    apply_rope,
+    rope_kv_store,
 )

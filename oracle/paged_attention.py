@@ -37,6 +37,14 @@ Readings where the pages are silent (each is listed in the design notes):
      lse_s = m_s + ln(l_s) is uniquely defined, m_s being a stabiliser.
   R8 decode rows with seq_len 0 are padding: their output is zero and their
      new-token location is -1 (a store skips negative locations).
+  R13 rotary pairs: interleaved (2i, 2i+1) by default, the pairing of a
+     complex-valued freqs_cis table read as consecutive real pairs; the
+     half-split pairing (i, i + D/2) is the alternative.
+  R14 the rotary table is freqs_cis[max_pos, D/2, 2] = (cos, sin) of the angle
+     of pair i at position p, given by the caller (P4, bullet on describing the
+     rotary table as cos/sin rather than a complex buffer).
+  R15 RoPE is applied to the new tokens' q and k before k is stored; v is
+     stored unrotated.
 """
 
 from __future__ import annotations
@@ -250,3 +258,52 @@ def prefill_attention(q, k_pool, v_pool, layer, req_to_token, req_pool_indices, 
                 out[t, h] = _softmax_attend(np.asarray(q[t, h], np.float64), K[:vis, h // g],
                                             V[:vis, h // g], scale)
     return out
+
+
+# ------------------------------------------------------- rotary + store
+
+def rope_pairs(D, interleaved):
+    """Index pairs (a_i, b_i), i < D/2, that one rotation angle acts on (R13):
+    interleaved (2i, 2i+1), the layout of a complex-valued frequency table
+    viewed as consecutive real pairs; otherwise half-split (i, i + D/2)."""
+    half = D // 2
+    if interleaved:
+        return [(2 * i, 2 * i + 1) for i in range(half)]
+    return [(i, i + half) for i in range(half)]
+
+
+def apply_rope(x, positions, freqs_cis, interleaved=True):
+    """Rotary position embedding of packed 3D rows (P1, bullet on extending the
+    rotary embedding to packed 3D inputs; P4, bullet on the cos/sin freqs_cis
+    table).
+
+    x: [T, H, D]; positions: [T] int; freqs_cis: [max_pos, D/2, 2] holding
+    (cos, sin) of the angle of pair i at each position (R14). Pair i of row t
+    is rotated by the angle of (positions[t], i):
+        a' = a cos - b sin,   b' = b cos + a sin.
+    Returns fp64 [T, H, D].
+    """
+    x = np.asarray(x, np.float64)
+    T, H, D = x.shape
+    out = x.copy()
+    for t in range(T):
+        p = int(positions[t])
+        for i, (a, b) in enumerate(rope_pairs(D, interleaved)):
+            c = float(freqs_cis[p, i, 0])
+            s = float(freqs_cis[p, i, 1])
+            out[t, :, a] = x[t, :, a] * c - x[t, :, b] * s
+            out[t, :, b] = x[t, :, b] * c + x[t, :, a] * s
+    return out
+
+
+def rope_kv_store(q, k_new, v_new, positions, freqs_cis, k_pool, v_pool, layer, loc,
+                  interleaved=True):
+    """RoPE on the new tokens' q and k, then the store of (rotated k, v) at the
+    cache locations (R15): returns (q_rot fp64 [T, Hq, D], k_pool', v_pool'),
+    where the pools are float64 copies with ``pool[layer, loc[t]]`` replaced for
+    every t with loc[t] >= 0 (R8) and every other entry unchanged."""
+    q_rot = apply_rope(q, positions, freqs_cis, interleaved)
+    k_rot = apply_rope(k_new, positions, freqs_cis, interleaved)
+    kp, vp = kv_store(np.asarray(k_pool, np.float64), np.asarray(v_pool, np.float64), layer,
+                      k_rot, np.asarray(v_new, np.float64), loc)
+    return q_rot, kp, vp

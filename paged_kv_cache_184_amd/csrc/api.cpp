@@ -212,6 +212,47 @@ pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_ne
                     "kv_store launch");
 }
 
+pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* q, void* q_out,
+                             int32_t n_q_heads, const void* k_new, const void* v_new,
+                             const int32_t* positions, const float* freqs_cis, int32_t max_pos,
+                             int32_t interleaved, const int32_t* loc, int64_t n_tokens,
+                             hipStream_t stream) {
+  pkv_status s;
+  if ((s = check_pool(pool, layer)) != PKV_OK) return s;
+  if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens must be >= 0");
+  if (n_tokens > (int64_t)1 << 40) return fail(PKV_EINVAL, "n_tokens too large");
+  if (interleaved != 0 && interleaved != 1) return fail(PKV_EINVAL, "interleaved must be 0 or 1");
+  if (max_pos <= 0) return fail(PKV_EINVAL, "max_pos must be > 0");
+  if ((q == nullptr) != (q_out == nullptr))
+    return fail(PKV_EINVAL, "q and q_out must both be set or both be NULL");
+  if (q && (s = check_heads(pool, n_q_heads)) != PKV_OK) return s;
+  if (n_tokens == 0) return ok();
+  if (!k_new || !v_new || !loc || !positions || !freqs_cis)
+    return fail(PKV_EINVAL, "k_new, v_new, positions, freqs_cis and loc are required");
+  if (!aligned16(k_new) || !aligned16(v_new) || (q && (!aligned16(q) || !aligned16(q_out))))
+    return fail(PKV_EALIGN, "q / q_out / k_new / v_new must be 16-byte aligned");
+  if (((uintptr_t)freqs_cis & 7) != 0) return fail(PKV_EALIGN, "freqs_cis must be 8-byte aligned");
+  pkv::RopeArgs r;
+  r.k_layer = a_k_layer(pool, layer);
+  r.v_layer = a_v_layer(pool, layer);
+  r.n_slots = pool->n_slots;
+  r.n_kv_heads = pool->n_kv_heads;
+  r.head_dim = pool->head_dim;
+  r.dtype = pool->dtype;
+  r.n_q_heads = q ? n_q_heads : 0;
+  r.q = q;
+  r.q_out = q_out;
+  r.k_new = k_new;
+  r.v_new = v_new;
+  r.positions = positions;
+  r.freqs_cis = freqs_cis;
+  r.max_pos = max_pos;
+  r.interleaved = interleaved;
+  r.loc = loc;
+  r.n_tokens = n_tokens;
+  return hip_status(pkv::launch_rope_kv_store(r, stream), "rope_kv_store launch");
+}
+
 pkv_status pkv_build_metadata(const pkv_batch_meta* meta, int32_t mode, pkv_split_cfg split,
                               int32_t* kv_indptr_out, int32_t* loc_out, int64_t loc_capacity,
                               int32_t* splits_out, hipStream_t stream) {

@@ -11,16 +11,18 @@
 // Partial kernel: one workgroup of kWaves waves per (request b, KV head, split
 // s); each wave takes a contiguous share (a multiple of 16 tokens) of the
 // split's tokens.
-//   * Lanes form 8 groups of 8; group t handles tokens t and t+8 of a 16-token
-//     tile, lane c of the group holds 16-byte chunks c, c+8, ... of the
+//   * Lanes form 64/LPR groups of LPR lanes (LPR = 8, or 16 for g >= 8 where
+//     the row allows); group t handles tokens t, t + 64/LPR, ... of a 16-token
+//     tile, lane c of the group holds 16-byte chunks c, c+LPR, ... of the
 //     token's K and V rows (D*es bytes per (slot, KV head)), so every load is a
-//     coalesced 16-byte gather and 8 lanes cover one row with full 128-byte
-//     segments.
+//     coalesced 16-byte gather and the lanes of a group cover one row with full
+//     128-byte segments. 16 lanes per row halve the per-lane q and accumulator
+//     registers, which at g >= 8 keeps them out of the AGPR file.
 //   * All g = Hq/Hkv query heads of the KV head are processed by the same wave,
 //     so each K/V byte is fetched from HBM once per request and reused g times
 //     from registers.
 //   * q.k: v_dot2_f32_bf16 on packed bf16 pairs (fp32 accumulate), then a
-//     3-step DPP reduction inside the 8-lane group.
+//     3-step (LPR = 8) or 4-step (LPR = 16) DPP reduction inside the group.
 //   * Online softmax in base 2 with a wave-uniform stabiliser m per head that
 //     is raised only when some score exceeds it by more than kTau (log2 units):
 //     until then exp2(x - m) <= 2^kTau, so no rescale of the accumulators is
@@ -50,50 +52,61 @@ constexpr float kTau = 8.0f;  // log2 headroom before the stabiliser is raised
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <typename T, int D>
+// Lanes per (slot, KV head) row: 8 in general; 16 for large groups (g >= 8)
+// when the row has at least 16 chunks, which halves the per-lane q and
+// accumulator registers (g heads x row elements per lane).
+template <typename T, int D, int G>
+constexpr int lanes_per_row() {
+  return (G >= 8 && D * elem_size<T>::value >= 256) ? 16 : 8;
+}
+
+template <typename T, int D, int LPR>
 struct Geo {
   static constexpr int ES = elem_size<T>::value;
-  static constexpr int ROW = D * ES;          // bytes of one (slot, KV head) row
-  static constexpr int CH = ROW / (8 * 16);  // 16-byte chunks per lane per token
-  static constexpr int EPC = 16 / ES;        // elements per chunk
-  static constexpr int E = CH * EPC;         // elements per lane per token (D / 8)
+  static constexpr int ROW = D * ES;            // bytes of one (slot, KV head) row
+  static constexpr int CH = ROW / (LPR * 16);   // 16-byte chunks per lane per token
+  static constexpr int EPC = 16 / ES;           // elements per chunk
+  static constexpr int E = CH * EPC;            // elements per lane per token (D / LPR)
+  static constexpr int GROUPS = 64 / LPR;       // token groups per wave
+  static constexpr int TPG = 16 / GROUPS;       // tokens per group per 16-token tile
   static_assert(CH >= 1 && CH <= 4, "row size");
+  static_assert(TPG % 2 == 0, "tokens of a group are paired for P.V");
 };
 
-template <typename T, int D>
+template <typename T, int D, int LPR>
 struct TileBuf {
-  u32x4 k[2][Geo<T, D>::CH];
-  u32x4 v[2][Geo<T, D>::CH];
+  u32x4 k[Geo<T, D, LPR>::TPG][Geo<T, D, LPR>::CH];
+  u32x4 v[Geo<T, D, LPR>::TPG][Geo<T, D, LPR>::CH];
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void load_tile(TileBuf<T, D>& buf, const char* kbase, const char* vbase,
-                                          int64_t row_stride, const int slot[2]) {
+template <typename T, int D, int LPR>
+__device__ __forceinline__ void load_tile(TileBuf<T, D, LPR>& buf, const char* kbase,
+                                          const char* vbase, int64_t row_stride,
+                                          const int (&slot)[Geo<T, D, LPR>::TPG]) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < Geo<T, D, LPR>::TPG; ++j) {
     const int64_t off = (int64_t)slot[j] * row_stride;
 #pragma unroll
-    for (int k = 0; k < Geo<T, D>::CH; ++k) {
-      buf.k[j][k] = *(const u32x4*)(kbase + off + 128 * k);
-      buf.v[j][k] = *(const u32x4*)(vbase + off + 128 * k);
+    for (int k = 0; k < Geo<T, D, LPR>::CH; ++k) {
+      buf.k[j][k] = *(const u32x4*)(kbase + off + 16 * LPR * k);
+      buf.v[j][k] = *(const u32x4*)(vbase + off + 16 * LPR * k);
     }
   }
 }
 
 // Partial dot product of this lane's elements of q (head h) and k.
-template <typename T, int D>
-__device__ __forceinline__ float lane_dot(const u32x4 (&q)[Geo<T, D>::CH],
-                                          const u32x4 (&k)[Geo<T, D>::CH]) {
+template <int CH, typename T>
+__device__ __forceinline__ float lane_dot(const u32x4 (&q)[CH], const u32x4 (&k)[CH]) {
   float acc = 0.f;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
-    for (int c = 0; c < Geo<T, D>::CH; ++c) {
+    for (int c = 0; c < CH; ++c) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) acc = dot2_bf16(q[c][w], k[c][w], acc);
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < Geo<T, D>::CH; ++c) {
+    for (int c = 0; c < CH; ++c) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) acc = fmaf(__uint_as_float(q[c][w]), __uint_as_float(k[c][w]), acc);
     }
@@ -102,8 +115,8 @@ __device__ __forceinline__ float lane_dot(const u32x4 (&q)[Geo<T, D>::CH],
 }
 
 // Element e (0..E-1) of a lane's row chunk set, as fp32.
-template <typename T, int D>
-__device__ __forceinline__ float elem(const u32x4 (&r)[Geo<T, D>::CH], int e) {
+template <int CH, typename T>
+__device__ __forceinline__ float elem(const u32x4 (&r)[CH], int e) {
   if constexpr (sizeof(T) == 2) {
     const uint32_t w = r[e / 8][(e % 8) / 2];
     return (e & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w);
@@ -112,34 +125,54 @@ __device__ __forceinline__ float elem(const u32x4 (&r)[Geo<T, D>::CH], int e) {
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int LPR>
 struct State {
-  float acc[G][Geo<T, D>::E];
+  float acc[G][Geo<T, D, LPR>::E];
   float l[G];
   float m[G];  // log2 units, wave-uniform
 };
 
-template <typename T, int D, int G>
-__device__ __forceinline__ void compute_tile(State<T, D, G>& st, const TileBuf<T, D>& buf,
-                                             const u32x4 (&q)[G][Geo<T, D>::CH], float scale2,
-                                             bool valid0, bool valid1) {
-  constexpr int E = Geo<T, D>::E;
-  float sc[G][2];
+// Sum over the LPR lanes of a row; every lane of the row gets the same bits.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+  x = sum8(x);
+  if constexpr (LPR == 16) x += dpp<kRowRor8>(x);
+  return x;
+}
+
+template <typename T, int D, int G, int LPR>
+__device__ __forceinline__ void compute_tile(State<T, D, G, LPR>& st, const TileBuf<T, D, LPR>& buf,
+                                             const u32x4 (&q)[G][Geo<T, D, LPR>::CH],
+                                             float scale2, const bool (&valid)[Geo<T, D, LPR>::TPG]) {
+  using Gm = Geo<T, D, LPR>;
+  constexpr int E = Gm::E;
+  constexpr int CH = Gm::CH;
+  constexpr int TPG = Gm::TPG;
+  float sc[G][TPG];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    // reduce unconditionally (all lanes active for the DPP moves), then mask
-    const float x0 = sum8(lane_dot<T, D>(q[h], buf.k[0])) * scale2;
-    const float x1 = sum8(lane_dot<T, D>(q[h], buf.k[1])) * scale2;
-    sc[h][0] = valid0 ? x0 : -INFINITY;
-    sc[h][1] = valid1 ? x1 : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) {
+      // reduce unconditionally (all lanes active for the DPP moves), then mask
+      const float x = row_sum<LPR>(lane_dot<CH, T>(q[h], buf.k[j])) * scale2;
+      sc[h][j] = valid[j] ? x : -INFINITY;
+    }
   }
   bool need = false;
 #pragma unroll
-  for (int h = 0; h < G; ++h) need |= fmaxf(sc[h][0], sc[h][1]) > st.m[h] + kTau;
+  for (int h = 0; h < G; ++h) {
+    float mx = sc[h][0];
+#pragma unroll
+    for (int j = 1; j < TPG; ++j) mx = fmaxf(mx, sc[h][j]);
+    need |= mx > st.m[h] + kTau;
+  }
   if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mnew = fmaxf(st.m[h], wave_max(fmaxf(sc[h][0], sc[h][1])));
+      float mx = sc[h][0];
+#pragma unroll
+      for (int j = 1; j < TPG; ++j) mx = fmaxf(mx, sc[h][j]);
+      const float mnew = fmaxf(st.m[h], wave_max(mx));
       const float corr = __builtin_amdgcn_exp2f(st.m[h] - mnew);
       st.l[h] *= corr;
 #pragma unroll
@@ -150,39 +183,43 @@ __device__ __forceinline__ void compute_tile(State<T, D, G>& st, const TileBuf<T
   if constexpr (sizeof(T) == 2) {
     // P.V on v_dot2_f32_bf16: P is rounded to bf16 (hardware round-to-nearest-
     // even) and the row sum takes the same rounded values; V needs no
-    // conversion, only pairing of the two tokens' values of each element.
-    uint32_t vp[E];
+    // conversion, only pairing of two tokens' values of each element.
 #pragma unroll
-    for (int k = 0; k < Geo<T, D>::CH; ++k)
+    for (int jp = 0; jp < TPG; jp += 2) {
+      uint32_t vp[E];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vp[k * 8 + 2 * w] = __builtin_amdgcn_perm(buf.v[1][k][w], buf.v[0][k][w], 0x05040100u);
-        vp[k * 8 + 2 * w + 1] = __builtin_amdgcn_perm(buf.v[1][k][w], buf.v[0][k][w], 0x07060302u);
+      for (int k = 0; k < CH; ++k)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vp[k * 8 + 2 * w] =
+              __builtin_amdgcn_perm(buf.v[jp + 1][k][w], buf.v[jp][k][w], 0x05040100u);
+          vp[k * 8 + 2 * w + 1] =
+              __builtin_amdgcn_perm(buf.v[jp + 1][k][w], buf.v[jp][k][w], 0x07060302u);
+        }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[h][jp] - st.m[h]);
+        const float p1 = __builtin_amdgcn_exp2f(sc[h][jp + 1] - st.m[h]);
+        const bf16x2_t pb = {(__bf16)p0, (__bf16)p1};
+        const uint32_t pp = __builtin_bit_cast(uint32_t, pb);
+        st.l[h] += bf16lo_to_f32(pp) + bf16hi_to_f32(pp);
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.acc[h][e] = dot2_bf16(pp, vp[e], st.acc[h][e]);
       }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
-      const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
-      const bf16x2_t pb = {(__bf16)p0, (__bf16)p1};
-      const uint32_t pp = __builtin_bit_cast(uint32_t, pb);
-      st.l[h] += bf16lo_to_f32(pp) + bf16hi_to_f32(pp);
-#pragma unroll
-      for (int e = 0; e < E; ++e) st.acc[h][e] = dot2_bf16(pp, vp[e], st.acc[h][e]);
     }
   } else {
-    float v0[E], v1[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      v0[e] = elem<T, D>(buf.v[0], e);
-      v1[e] = elem<T, D>(buf.v[1], e);
-    }
+    for (int j = 0; j < TPG; ++j) {
+      float v[E];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[h][0] - st.m[h]);
-      const float p1 = __builtin_amdgcn_exp2f(sc[h][1] - st.m[h]);
-      st.l[h] += p0 + p1;
+      for (int e = 0; e < E; ++e) v[e] = elem<CH, T>(buf.v[j], e);
 #pragma unroll
-      for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(p1, v1[e], fmaf(p0, v0[e], st.acc[h][e]));
+      for (int h = 0; h < G; ++h) {
+        const float p = __builtin_amdgcn_exp2f(sc[h][j] - st.m[h]);
+        st.l[h] += p;
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.acc[h][e] = fmaf(p, v[e], st.acc[h][e]);
+      }
     }
   }
 }
@@ -196,17 +233,21 @@ constexpr int kSuper = 16 * kTiles;
 // ahead of its use, so the wait counts are static and no tile buffer is carried
 // around a loop. Positions past ce re-read the last valid token (cache hits)
 // and are masked.
-template <typename T, int D, int G, int NT>
-__device__ __forceinline__ void tile_run(State<T, D, G>& st, const int* slots, int cb, int ce,
+template <typename T, int D, int G, int LPR, int NT>
+__device__ __forceinline__ void tile_run(State<T, D, G, LPR>& st, const int* slots, int cb, int ce,
                                          int grp, const char* kbase, const char* vbase,
-                                         int64_t row_stride, const u32x4 (&q)[G][Geo<T, D>::CH],
-                                         float scale2) {
-  TileBuf<T, D> buf[3];
+                                         int64_t row_stride,
+                                         const u32x4 (&q)[G][Geo<T, D, LPR>::CH], float scale2) {
+  using Gm = Geo<T, D, LPR>;
+  constexpr int TPG = Gm::TPG;
+  constexpr int GR = Gm::GROUPS;
+  TileBuf<T, D, LPR> buf[3];
+  // token j of group grp in tile i is cb + 16 i + grp + GR j
   auto issue = [&](int i) {
-    int sl[2];
+    int sl[TPG];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sl[j] = slots[min(16 * i + grp + 8 * j, ce - cb - 1)];
-    load_tile<T, D>(buf[i % 3], kbase, vbase, row_stride, sl);
+    for (int j = 0; j < TPG; ++j) sl[j] = slots[min(16 * i + grp + GR * j, ce - cb - 1)];
+    load_tile<T, D, LPR>(buf[i % 3], kbase, vbase, row_stride, sl);
   };
   issue(0);
   if (NT > 1) issue(1);
@@ -214,25 +255,32 @@ __device__ __forceinline__ void tile_run(State<T, D, G>& st, const int* slots, i
   for (int i = 0; i < NT; ++i) {
     if (i + 2 < NT) issue(i + 2);
     const int t = cb + 16 * i + grp;
-    compute_tile<T, D, G>(st, buf[i % 3], q, scale2, t < ce, t + 8 < ce);
+    bool valid[TPG];
+#pragma unroll
+    for (int j = 0; j < TPG; ++j) valid[j] = t + GR * j < ce;
+    compute_tile<T, D, G, LPR>(st, buf[i % 3], q, scale2, valid);
   }
 }
 
-template <typename T, int D, int G>
-__device__ __forceinline__ void super_tile(State<T, D, G>& st, const int* slots, int cb, int ce,
-                                           int grp, const char* kbase, const char* vbase,
-                                           int64_t row_stride, const u32x4 (&q)[G][Geo<T, D>::CH],
+template <typename T, int D, int G, int LPR>
+__device__ __forceinline__ void super_tile(State<T, D, G, LPR>& st, const int* slots, int cb,
+                                           int ce, int grp, const char* kbase, const char* vbase,
+                                           int64_t row_stride,
+                                           const u32x4 (&q)[G][Geo<T, D, LPR>::CH],
                                            float scale2) {
   if constexpr (sizeof(T) == 4) {
     // fp32 inputs: one tile at a time (no cross-tile prefetch); a precision
     // path, not a bandwidth path
     for (int t0 = cb; t0 < ce; t0 += 16)
-      tile_run<T, D, G, 1>(st, slots + (t0 - cb), t0, ce, grp, kbase, vbase, row_stride, q, scale2);
+      tile_run<T, D, G, LPR, 1>(st, slots + (t0 - cb), t0, ce, grp, kbase, vbase, row_stride, q,
+                                scale2);
     return;
   }
   switch (ceil_div(ce - cb, 16)) {
-#define PKV_RUN(n) \
-  case n: tile_run<T, D, G, n>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2); break;
+#define PKV_RUN(n)                                                                             \
+  case n:                                                                                      \
+    tile_run<T, D, G, LPR, n>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2);    \
+    break;
     PKV_RUN(1) PKV_RUN(2) PKV_RUN(3) PKV_RUN(4) PKV_RUN(5) PKV_RUN(6) PKV_RUN(7) PKV_RUN(8)
 #undef PKV_RUN
     default: break;
@@ -298,7 +346,8 @@ __device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
 //     splits leave partials for the merge kernel.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
-  using Gm = Geo<T, D>;
+  constexpr int LPR = lanes_per_row<T, D, G>();
+  using Gm = Geo<T, D, LPR>;
   constexpr int CH = Gm::CH;
   constexpr int E = Gm::E;
   __shared__ int slot_lds[kWaves][kSuper];
@@ -308,8 +357,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int grp = lane >> 3;
-  const int c = lane & 7;
+  const int grp = lane / LPR;  // token group
+  const int c = lane % LPR;    // this lane's first 16-byte chunk of a row
   const int s = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -361,6 +410,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW + 16 * c;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW + 16 * c;
+  // chunk k of this lane is row chunk c + LPR k
 
   // slot ids of the first super-tile: two per lane, issued before anything waits
   int ids[2];
@@ -375,10 +425,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int k = 0; k < CH; ++k) q[h][k] = *(const u32x4*)(qbase + (int64_t)h * Gm::ROW + 128 * k);
+    for (int k = 0; k < CH; ++k)
+      q[h][k] = *(const u32x4*)(qbase + (int64_t)h * Gm::ROW + 16 * LPR * k);
 
   const float scale2 = a.scale * kLog2e;
-  State<T, D, G> st;
+  State<T, D, G, LPR> st;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     st.l[h] = 0.f;
@@ -400,34 +451,33 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 #pragma unroll
       for (int j = 0; j < 2; ++j) ids[j] = row[min(nb + lane + 64 * j, whi - 1)];
     }
-    super_tile<T, D, G>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2);
+    super_tile<T, D, G, LPR>(st, slots, cb, ce, grp, kbase, vbase, row_stride, q, scale2);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
   }
 
-  // Reduce over the 8 token groups: lanes with equal c hold the same elements.
+  // Reduce over the token groups: lanes with equal c hold the same elements
+  // (lanes c + LPR grp; with LPR = 8, row_ror:8 first pairs the groups of a row).
+  auto over_groups = [&](float x) {
+    if constexpr (LPR == 8) x += dpp<kRowRor8>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+  };
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    st.l[h] += dpp<kRowRor8>(st.l[h]);
-    st.l[h] += __shfl_xor(st.l[h], 16);
-    st.l[h] += __shfl_xor(st.l[h], 32);
+    st.l[h] = over_groups(st.l[h]);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float x = st.acc[h][e];
-      x += dpp<kRowRor8>(x);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      st.acc[h][e] = x;
-    }
+    for (int e = 0; e < E; ++e) st.acc[h][e] = over_groups(st.acc[h][e]);
   }
   // Hand the wave's (m, l, acc) to LDS; an empty wave leaves m = -inf, l = 0, acc = 0.
-  if (lane < 8) {
+  if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int k = 0; k < CH; ++k)
 #pragma unroll
         for (int e = 0; e < Gm::EPC; ++e)
-          red_acc[wave][h][(c + 8 * k) * Gm::EPC + e] = st.acc[h][k * Gm::EPC + e];
+          red_acc[wave][h][(c + LPR * k) * Gm::EPC + e] = st.acc[h][k * Gm::EPC + e];
   }
   if (lane == 0) {
 #pragma unroll

@@ -75,6 +75,28 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+struct RopeArgs {
+  void* k_layer;  // pools at the layer
+  void* v_layer;
+  int64_t n_slots;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int32_t n_q_heads;  // 0 when q is not rotated
+  const void* q;      // [T, Hq, D] or null
+  void* q_out;        // may equal q
+  const void* k_new;  // [T, Hkv, D]
+  const void* v_new;
+  const int32_t* positions;  // [T]
+  const float* freqs_cis;    // [max_pos, D/2, 2]
+  int32_t max_pos;
+  int32_t interleaved;
+  const int32_t* loc;  // [T]
+  int64_t n_tokens;
+};
+
+hipError_t launch_rope_kv_store(const RopeArgs& r, hipStream_t stream);
+
 // Supported group sizes / head dims (the dispatch tables in the kernels match these).
 inline bool group_supported(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 inline bool head_dim_supported(int d) { return d == 64 || d == 128; }

@@ -127,6 +127,36 @@ def kv_store(k_pool, v_pool, layer: int, k_new, v_new, loc, stream=None) -> None
                               loc.data_ptr(), n, _stream(stream)))
 
 
+def rope_kv_store(k_pool, v_pool, layer: int, k_new, v_new, positions, freqs_cis, loc,
+                  q=None, q_out=None, interleaved: bool = True, stream=None) -> None:
+    """Rotary embedding of the new tokens fused with their store
+    (pkv_rope_kv_store): pool[layer, loc[t]] = (rope(k_new[t]), v_new[t]) and,
+    when q is given, q_out = rope(q) (q_out defaults to q: in place)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "dtype mismatch")
+    _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
+    _need(loc.dtype == torch.int32 and loc.is_contiguous(), "loc must be contiguous int32")
+    _need(positions.dtype == torch.int32 and positions.is_contiguous(),
+          "positions must be contiguous int32")
+    _need(freqs_cis.dtype == torch.float32 and freqs_cis.is_contiguous() and
+          freqs_cis.dim() == 3 and freqs_cis.shape[1:] == (k_pool.shape[3] // 2, 2),
+          "freqs_cis must be contiguous float32 [max_pos, head_dim/2, 2]")
+    n = loc.shape[0]
+    _need(positions.shape[0] == n, "positions shape")
+    _need(k_new.numel() == n * k_pool.shape[2] * k_pool.shape[3], "k_new shape")
+    _need(v_new.numel() == k_new.numel(), "v_new shape")
+    hq = 0
+    if q is not None:
+        q_out = q if q_out is None else q_out
+        _need(q.dtype == k_pool.dtype and q.is_contiguous() and q_out.is_contiguous(), "q layout")
+        _need(q.shape[0] == n and q_out.shape == q.shape, "q shape")
+        hq = q.shape[1]
+    _check(lib().pkv_rope_kv_store(C.byref(pool), layer, _ptr(q), _ptr(q_out), hq,
+                                   k_new.data_ptr(), v_new.data_ptr(), positions.data_ptr(),
+                                   freqs_cis.data_ptr(), freqs_cis.shape[0],
+                                   1 if interleaved else 0, loc.data_ptr(), n, _stream(stream)))
+
+
 def build_metadata(meta: BatchMeta, mode: int, split: Optional[SplitCfg] = None,
                    kv_indptr_out=None, loc_out=None, splits_out=None, stream=None) -> None:
     """Index step (pkv_build_metadata)."""

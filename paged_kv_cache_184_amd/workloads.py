@@ -241,15 +241,22 @@ def packed_prefill(n_layers: int = 1, n_req: int = 8) -> PagedBatch:
                    1.0 / np.sqrt(128.0), lens, n_new, lists, rng)
 
 
-def large_batch_decode(n_layers: int = 1, sigma: float = 1.0) -> PagedBatch:
+def large_batch_decode(n_layers: int = 1, sigma: float = 1.0,
+                       layout: str = "fragmented") -> PagedBatch:
     """B=64, 64 q / 8 KV heads, head_dim 128, bf16; L = min(32768, max(1, round(4096 exp(sigma Z))));
-    2^21-slot pool with token-granular (fragmented) slot assignment."""
+    2^21-slot pool with token-granular (fragmented) slot assignment, or, for
+    comparison, the same lengths in shuffled 16-token pages."""
     k = 5
     rng = np.random.default_rng(SEED_BASE + k + 1)
     n_slots = 1 << 21
     z = rng.standard_normal(64)
     lens = np.minimum(32768, np.maximum(1, np.rint(4096.0 * np.exp(sigma * z)))).astype(np.int64)
-    lists = _fragmented_slots(rng, n_slots, lens, reserve=1)
+    if layout == "fragmented":
+        lists = _fragmented_slots(rng, n_slots, lens, reserve=1)
+    elif layout == "pages16":
+        lists = _pages16_slots(rng, n_slots, lens, reserve=PAGE)
+    else:
+        raise ValueError(layout)
     return _finish("large_batch_decode", n_layers, n_slots, 64, 8, 128, "bf16",
                    1.0 / np.sqrt(128.0), lens, np.ones(64, np.int32), lists, rng)
 
@@ -287,6 +294,17 @@ def custom(name: str, *, n_layers: int, n_slots: int, n_q_heads: int, n_kv_heads
         scale = 1.0 / np.sqrt(head_dim)
     return _finish(name, n_layers, n_slots, n_q_heads, n_kv_heads, head_dim, dtype, scale,
                    seq_lens, n_new, lists, rng, stride=stride, n_rows=n_rows)
+
+
+def rope_freqs_cis(max_pos: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """Input table for the rotary step: float32 [max_pos, head_dim/2, 2] holding
+    (cos, sin) of angle p * base^(-2i/head_dim) for position p and pair i (the
+    conventional frequency schedule; the library and the oracle both take the
+    table as given)."""
+    half = head_dim // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

@@ -355,10 +355,107 @@ def pin_kv_store_bytes(O, seed=14):
                 assert v2[L, s].tobytes() == vp[L, s].tobytes()
 
 
+def pin_rope_golden(O):
+    g = golden()["rope"]
+    x = np.array(g["x"], np.float64)
+    tab = np.array(g["table"], np.float64)
+    pos = np.array(g["position"])
+    assert np.allclose(O.apply_rope(x, pos, tab, True), np.array(g["interleaved_out"]), atol=1e-12)
+    assert np.allclose(O.apply_rope(x, pos, tab, False), np.array(g["half_split_out"]),
+                       atol=1e-12)
+
+
+def pin_rope_complex(O, seed=20):
+    """Interleaved rotation of pair i equals the complex product
+    (x_2i + j x_2i+1) * (cos + j sin), for any table (numpy complex arithmetic)."""
+    rng = np.random.default_rng(seed)
+    T, H, D, P = 5, 3, 8, 7
+    x = rng.standard_normal((T, H, D))
+    tab = rng.standard_normal((P, D // 2, 2))
+    pos = rng.integers(0, P, size=T)
+    got = O.apply_rope(x, pos, tab, True)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    w = tab[pos, :, 0] + 1j * tab[pos, :, 1]
+    r = z * w[:, None, :]
+    want = np.empty_like(x)
+    want[..., 0::2] = r.real
+    want[..., 1::2] = r.imag
+    assert np.allclose(got, want, atol=1e-12)
+
+
+def pin_rope_half_split_is_permuted_interleaved(O, seed=21):
+    """Half-split pairs (i, i+D/2) are the interleaved pairs (2i, 2i+1) after the
+    permutation that moves element i to 2i and i+D/2 to 2i+1."""
+    rng = np.random.default_rng(seed)
+    T, H, D, P = 4, 2, 8, 6
+    x = rng.standard_normal((T, H, D))
+    tab = rng.standard_normal((P, D // 2, 2))
+    pos = rng.integers(0, P, size=T)
+    perm = np.empty(D, dtype=np.int64)  # interleaved position of each half-split element
+    perm[: D // 2] = 2 * np.arange(D // 2)
+    perm[D // 2:] = 2 * np.arange(D // 2) + 1
+    xi = np.empty_like(x)
+    xi[..., perm] = x
+    yi = O.apply_rope(xi, pos, tab, True)
+    assert np.allclose(O.apply_rope(x, pos, tab, False), yi[..., perm], atol=1e-12)
+
+
+def pin_rope_standard_table(O, seed=22):
+    """With the conventional table: position 0 is the identity, pair norms are
+    kept, and q.k after rotation depends only on the position difference."""
+    rng = np.random.default_rng(seed)
+    D = 16
+    tab = W.rope_freqs_cis(64, D).astype(np.float64)
+    x = rng.standard_normal((3, 2, D))
+    assert np.allclose(O.apply_rope(x, np.zeros(3, int), tab, True), x, atol=1e-12)
+    y = O.apply_rope(x, np.array([5, 17, 40]), tab, False)
+    for a, b in O.rope_pairs(D, False):
+        assert np.allclose(y[..., a] ** 2 + y[..., b] ** 2, x[..., a] ** 2 + x[..., b] ** 2,
+                           atol=1e-9)
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    for inter in (True, False):
+        d1 = float((O.apply_rope(q, [9], tab, inter) * O.apply_rope(k, [4], tab, inter)).sum())
+        d2 = float((O.apply_rope(q, [30], tab, inter) * O.apply_rope(k, [25], tab, inter)).sum())
+        assert abs(d1 - d2) < 1e-5  # the table is float32
+
+
+def pin_rope_kv_store(O, seed=23):
+    """Rotated k and unrotated v land at the locations; nothing else changes."""
+    rng = np.random.default_rng(seed)
+    T, Hq, Hkv, D, S = 4, 4, 2, 8, 20
+    q = rng.standard_normal((T, Hq, D))
+    k = rng.standard_normal((T, Hkv, D))
+    v = rng.standard_normal((T, Hkv, D))
+    tab = rng.standard_normal((9, D // 2, 2))
+    pos = np.array([3, 0, 8, 5])
+    kp = rng.standard_normal((2, S, Hkv, D))
+    vp = rng.standard_normal((2, S, Hkv, D))
+    loc = np.array([7, -1, 19, 2], np.int32)
+    q_rot, k2, v2 = O.rope_kv_store(q, k, v, pos, tab, kp, vp, 1, loc, interleaved=True)
+    assert np.allclose(q_rot, O.apply_rope(q, pos, tab, True), atol=0)
+    # hand-rolled rotation of the stored k rows, pair by pair
+    for t, s in enumerate(loc):
+        if s < 0:
+            continue
+        c, sn = tab[pos[t], :, 0], tab[pos[t], :, 1]
+        want = np.empty((Hkv, D))
+        want[:, 0::2] = k[t][:, 0::2] * c - k[t][:, 1::2] * sn
+        want[:, 1::2] = k[t][:, 1::2] * c + k[t][:, 0::2] * sn
+        assert np.allclose(k2[1, s], want, atol=1e-12)
+        assert np.array_equal(v2[1, s], v[t])
+    keep = np.ones(S, bool)
+    keep[[7, 19, 2]] = False
+    assert np.array_equal(k2[0], kp[0]) and np.array_equal(v2[0], vp[0])
+    assert np.array_equal(k2[1, keep], kp[1, keep]) and np.array_equal(v2[1, keep], vp[1, keep])
+
+
 ALL_PINS = [
     pin_decode_vs_sdpa, pin_prefill_vs_sdpa, pin_golden_two_keys, pin_golden_prefill,
     pin_closed_forms, pin_gqa_mapping, pin_slot_permutation, pin_split_merge,
     pin_lse_merge_closed_form, pin_decode_equals_prefill_one_token, pin_causal_dependence,
     pin_scale, pin_padded_rows, pin_index_golden, pin_kv_indptr_properties, pin_split_golden,
-    pin_split_properties, pin_kv_store_golden, pin_kv_store_bytes,
+    pin_split_properties, pin_kv_store_golden, pin_kv_store_bytes, pin_rope_golden,
+    pin_rope_complex, pin_rope_half_split_is_permuted_interleaved, pin_rope_standard_table,
+    pin_rope_kv_store,
 ]

@@ -103,6 +103,34 @@ def test_kv_store_other_rejects(lib):
     assert lib.pkv_last_error() == b""
 
 
+def test_rope_kv_store_rejects(lib):
+    p = _pool()
+    f = lib.pkv_rope_kv_store
+
+    def call(pool=p, layer=0, q=16, q_out=16, hq=4, k=16, v=16, pos=16, tab=8, max_pos=4,
+             inter=1, loc=16, n=1):
+        return f(C.byref(pool) if pool is not None else None, layer, q, q_out, hq, k, v, pos, tab,
+                 max_pos, inter, loc, n, None)
+
+    assert call(pool=None) == _lib.PKV_EINVAL
+    assert call(n=-1) == _lib.PKV_EINVAL
+    assert call(inter=2) == _lib.PKV_EINVAL
+    assert call(max_pos=0) == _lib.PKV_EINVAL
+    assert call(q_out=None) == _lib.PKV_EINVAL  # q without q_out
+    assert call(hq=3) == _lib.PKV_ESHAPE        # not a multiple of n_kv_heads
+    assert call(k=None) == _lib.PKV_EINVAL
+    assert call(tab=None) == _lib.PKV_EINVAL
+    assert call(pos=None) == _lib.PKV_EINVAL
+    assert call(k=24) == _lib.PKV_EALIGN
+    assert call(q=24, q_out=24) == _lib.PKV_EALIGN
+    assert call(tab=4) == _lib.PKV_EALIGN
+    assert call(layer=9) != _lib.PKV_OK
+    # zero tokens is a successful no-op
+    assert call(q=None, q_out=None, k=None, v=None, pos=None, tab=None, loc=None,
+                n=0) == _lib.PKV_OK
+    assert lib.pkv_last_error() == b""
+
+
 def _decode(lib, pool=None, layer=0, q=16, hq=4, meta=None, scale=0.125, split=None, ws=256,
             ws_bytes=1 << 20, out=16, fn="pkv_paged_decode_attn"):
     pool = pool or _pool()

@@ -38,6 +38,20 @@ MUTATIONS = {
     "store_negative_loc": ("if loc[t] >= 0:", "if True:"),
     "lse_drops_max": ("lse[h, s] = m + np.log(p.sum())", "lse[h, s] = np.log(p.sum())"),
     "padded_row_nonzero_loc": ("if L > 0 else -1", "if L > 0 else 0"),
+    "rope_sin_sign": ("out[t, :, a] = x[t, :, a] * c - x[t, :, b] * s",
+                      "out[t, :, a] = x[t, :, a] * c + x[t, :, b] * s"),
+    "rope_reads_rotated_a": ("out[t, :, b] = x[t, :, b] * c + x[t, :, a] * s",
+                             "out[t, :, b] = x[t, :, b] * c + out[t, :, a] * s"),
+    "rope_pairs_swapped": ("return [(2 * i, 2 * i + 1) for i in range(half)]",
+                           "return [(2 * i + 1, 2 * i) for i in range(half)]"),
+    "rope_half_split_adjacent": ("return [(i, i + half) for i in range(half)]",
+                                 "return [(2 * i, 2 * i + 1) for i in range(half)]"),
+    "rope_cos_for_sin": ("s = float(freqs_cis[p, i, 1])", "s = float(freqs_cis[p, i, 0])"),
+    "rope_position_ignored": ("p = int(positions[t])", "p = 0"),
+    "rope_store_unrotated_k": ("layer,\n                      k_rot, np.asarray(v_new",
+                               "layer,\n                      np.asarray(k_new, np.float64), np.asarray(v_new"),
+    "rope_q_unrotated": ("q_rot = apply_rope(q, positions, freqs_cis, interleaved)",
+                         "q_rot = np.asarray(q, np.float64)"),
 }
 
 
