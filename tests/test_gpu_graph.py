@@ -1,0 +1,140 @@
+"""GPU: a whole decode step captured once into a HIP graph and replayed over
+several steps with its metadata updated in place between replays.
+
+The step is the index step (kv_indptr, new-token locations, split counts), the
+rotary embedding of the new tokens' q / k fused with their store, and the
+split-KV attention with its merge. Between replays only device buffers change
+(seq_lens += 1, positions, the new tokens' q / k / v), as an engine keeps
+fixed-capacity metadata and rewrites it every step. Every replay must match the
+same calls run eagerly on a twin of the state, bit for bit (outputs and both
+pools), and the oracle within tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from paged_kv_cache_184_amd import ops
+from paged_kv_cache_184_amd import workloads as W
+from tests.gpu_util import DEV, compare, say
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 5
+
+
+class StepState:
+    """Device buffers of one decode step whose addresses stay fixed."""
+
+    def __init__(self, b, vals, r2t, tab, split, ws_slots):
+        dt = torch.bfloat16
+        self.b = b
+        self.r2t = torch.from_numpy(r2t).to(DEV)
+        self.rows = torch.from_numpy(b.req_pool_indices).to(DEV)
+        self.lens = torch.from_numpy(b.seq_lens.copy()).to(DEV)
+        self.pos = (self.lens - 1).to(torch.int32)
+        self.q = torch.empty((b.batch, b.n_q_heads, b.head_dim), dtype=dt, device=DEV)
+        self.k_new = torch.empty((b.batch, b.n_kv_heads, b.head_dim), dtype=dt, device=DEV)
+        self.v_new = torch.empty_like(self.k_new)
+        self.k_pool = torch.from_numpy(vals.k_pool).to(DEV, dt)
+        self.v_pool = torch.from_numpy(vals.v_pool).to(DEV, dt)
+        self.tab = torch.from_numpy(tab).to(DEV)
+        self.kv_indptr = torch.empty(b.batch + 1, dtype=torch.int32, device=DEV)
+        self.loc = torch.empty(b.batch, dtype=torch.int32, device=DEV)
+        self.splits = torch.empty(b.batch, dtype=torch.int32, device=DEV)
+        self.split = split
+        self.ws = ops.alloc_decode_workspace(b.batch, b.n_q_heads, b.head_dim, split.max_splits)
+        self.out = torch.empty_like(self.q)
+        self.meta = ops.make_meta(self.r2t, self.rows, self.lens)
+        self.calls = [
+            ops.prepare_metadata(self.meta, ops.PKV_MODE_DECODE, split, self.kv_indptr, self.loc,
+                                 self.splits),
+            lambda: ops.rope_kv_store(self.k_pool, self.v_pool, 0, self.k_new, self.v_new,
+                                      self.pos, self.tab, self.loc, q=self.q),
+            ops.prepare_decode(self.q, self.k_pool, self.v_pool, 0, self.meta, b.scale, split,
+                               self.ws, self.out, stage="all"),
+        ]
+
+    def run(self):
+        for c in self.calls:
+            c()
+
+    def advance(self, q, k, v):
+        """Next step: one more key per request, new token values."""
+        self.lens.add_(1)
+        self.pos.copy_(self.lens - 1)
+        self.q.copy_(q)
+        self.k_new.copy_(k)
+        self.v_new.copy_(v)
+
+
+def test_decode_step_graph_replay_with_in_place_metadata():
+    # ragged lengths with room for STEPS more tokens per request
+    lens0 = np.array([700, 33, 1500, 255, 16, 900, 64, 1201])
+    b = W.custom("graph_steps", n_layers=1, n_slots=1 << 14, n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens0, n_new=np.ones(8, np.int64),
+                 seed=400, stride=int(lens0.max()) + STEPS + 8)
+    vals = W.host_values(b, 401)
+    # fresh slots for the STEPS new positions of every request (outside every live slot)
+    r2t = b.req_to_token.copy()
+    free = np.setdiff1d(np.arange(b.n_slots - 1), b.live_slots)
+    rng = np.random.default_rng(402)
+    fresh = rng.permutation(free)[: b.batch * STEPS].reshape(b.batch, STEPS)
+    for i in range(b.batch):
+        r = b.req_pool_indices[i]
+        r2t[r, lens0[i]: lens0[i] + STEPS] = fresh[i]
+        # position lens0-1 (this step's token) already has a slot from the batch
+    tab = W.rope_freqs_cis(int(lens0.max()) + STEPS + 1, 128)
+    split = ops.split_cfg(8, 0, 256)
+
+    A = StepState(b, vals, r2t, tab, split, None)
+    B = StepState(b, vals, r2t, tab, split, None)
+    inputs = []
+    for s in range(STEPS + 1):
+        inputs.append(tuple(torch.from_numpy(W.normal_values(shape, 410 + 3 * s + j, "bf16"))
+                            .to(DEV, torch.bfloat16)
+                            for j, shape in enumerate([(b.batch, 32, 128), (b.batch, 8, 128),
+                                                       (b.batch, 8, 128)])))
+    # warm-up and capture on A (the captured step is step 0's state)
+    q0, k0, v0 = inputs[0]
+    for st in (A, B):
+        st.q.copy_(q0), st.k_new.copy_(k0), st.v_new.copy_(v0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        A.calls[0]()  # metadata only: leaves the pools as they are
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.run()
+    torch.cuda.synchronize()
+
+    for step in range(STEPS):
+        say(f"graph step {step}")
+        if step > 0:
+            qs, ks, vs = inputs[step]
+            A.advance(qs, ks, vs)
+            B.advance(qs, ks, vs)
+        A.out.zero_()
+        g.replay()
+        B.run()
+        torch.cuda.synchronize()
+        assert torch.equal(A.out.view(torch.int16), B.out.view(torch.int16)), step
+        assert torch.equal(A.loc, B.loc) and torch.equal(A.kv_indptr, B.kv_indptr), step
+        assert torch.equal(A.k_pool.view(torch.int16), B.k_pool.view(torch.int16)), step
+        assert torch.equal(A.v_pool.view(torch.int16), B.v_pool.view(torch.int16)), step
+        _ = (A.q.float() * 2).sum().item()  # unrelated eager work between replays
+        # index step against the oracle, bit-exact
+        lens = lens0 + step
+        assert np.array_equal(A.kv_indptr.cpu().numpy(), O.kv_indptr(lens))
+        assert np.array_equal(A.loc.cpu().numpy(),
+                              O.decode_locations(r2t, b.req_pool_indices, lens))
+        if step in (0, STEPS - 1):
+            # attention against the oracle on the device pools (rotated q as input)
+            kp = A.k_pool.float().cpu().numpy()
+            vp = A.v_pool.float().cpu().numpy()
+            ref = O.decode_attention(A.q.float().cpu().numpy(), kp, vp, 0, r2t,
+                                     b.req_pool_indices, lens, b.scale)
+            compare(A.out.float().cpu().numpy(), ref, "bf16", f"graph step {step}")
