@@ -335,7 +335,8 @@ __device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
   __syncthreads();
 }
 
-// One workgroup per (request b, KV head, split s). Optional fused steps:
+// One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B).
+// Optional fused steps:
 //   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
 //     index step for the whole batch;
 //   a.k_new / v_new: the wave whose share holds position L-1 first stores the
@@ -359,8 +360,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int lane = tid & 63;
   const int grp = lane / LPR;  // token group
   const int c = lane % LPR;    // this lane's first 16-byte chunk of a row
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
+  // KV head fastest: workgroups go to the XCDs round-robin by linear id, so
+  // each XCD gets the same KV head(s) of every split of every request, and
+  // requests with few splits do not pile their work onto a few XCDs.
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
 
   if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D>
 hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
-  dim3 grid(a.split.max_splits, a.n_kv_heads, a.batch);
+  dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
   switch (g) {
     case 1: decode_partial_kernel<T, D, 1><<<grid, 64 * kWaves, 0, stream>>>(a); break;
     case 2: decode_partial_kernel<T, D, 2><<<grid, 64 * kWaves, 0, stream>>>(a); break;
