@@ -335,6 +335,103 @@ __device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
   __syncthreads();
 }
 
+// What a split workgroup needs to know about its request and token range.
+struct SplitCtx {
+  int L, S, chunk, lo, hi;
+  int64_t row_stride;   // bytes between consecutive slots of one pool layer
+  const int32_t* row;   // req_to_token row of the request
+  int n_slots;
+};
+
+// Request length, split plan and this split's token range. Returns false when
+// the workgroup has no split to compute (after zeroing a padded request's
+// output rows when an output is given).
+template <typename T, int D, int G, int NT>
+__device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh, int s,
+                                            SplitCtx& c) {
+  constexpr int ROW = D * elem_size<T>::value;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+  c.L = L;
+  c.S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens, &c.chunk);
+  if (s >= c.S) {
+    // a padded request (L = 0) has no split: its rows are zero
+    if (c.S == 0 && s == 0 && a.out)
+      for (int i = threadIdx.x; i < G * D; i += NT)
+        store_out<T>(a.out, ((int64_t)b * a.n_q_heads + kvh * G) * D + i, 0.f);
+    return false;
+  }
+  c.lo = s * c.chunk;
+  c.hi = min(L, c.lo + c.chunk);
+  const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
+  c.row = a.req_to_token + (int64_t)r * a.stride;
+  c.n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
+  c.row_stride = (int64_t)a.n_kv_heads * ROW;
+  return true;
+}
+
+// Store of the new token (position L-1) of this KV head by the wave whose
+// share [wlo, whi) holds it, completed before that wave reads it back.
+template <typename T, int D>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const SplitCtx& c, int b,
+                                                int kvh, int wlo, int whi, int lane) {
+  constexpr int ROW = D * elem_size<T>::value;
+  if (!a.k_new || c.L - 1 < wlo || c.L - 1 >= whi) return;
+  const int raw = c.row[c.L - 1];
+  constexpr int CPR = ROW / 16;  // 16-byte chunks of one (slot, KV head) row
+  if (raw >= 0 && raw < c.n_slots && lane < 2 * CPR) {
+    const int chk = lane % CPR;
+    const char* src = (const char*)(lane < CPR ? a.k_new : a.v_new) +
+                      ((int64_t)b * a.n_kv_heads + kvh) * ROW + 16 * chk;
+    char* dst = (char*)(lane < CPR ? a.k : a.v) + (int64_t)raw * c.row_stride +
+                (int64_t)kvh * ROW + 16 * chk;
+    *(u32x4*)dst = *(const u32x4*)src;
+  }
+  // the row is read back below by this same wave: complete the stores first
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Merge the W waves' (m, l, acc) from LDS (fixed order) into the split's
+// normalised output: written directly for a single-split request when an
+// output is given, else as the split's partial (o, (m ln2, l)).
+template <typename T, int D, int G, int W>
+__device__ __forceinline__ void finish_split(const DecodeArgs& a, const float (*red_acc)[G][D],
+                                             const float (*red_ml)[G][2], int b, int kvh, int s,
+                                             int S) {
+  const int qh0 = kvh * G;
+  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits;
+  const bool direct = a.out != nullptr && S == 1;
+  for (int i = threadIdx.x; i < G * D; i += 64 * W) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, red_ml[w][h][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = red_ml[w][h][0];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      num = fmaf(f, red_acc[w][h][d], num);
+      den = fmaf(f, red_ml[w][h][1], den);
+    }
+    const float o = num / den;
+    if (direct) {
+      store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0 + h) * D + d, o);
+      continue;
+    }
+    const int64_t part = part0 + (int64_t)h * a.split.max_splits + s;
+    a.o_part[part * D + d] = o;
+    if (d == 0) {
+      float2 ml;
+      ml.x = M * kLn2;
+      ml.y = den;
+      *(float2*)(a.ml_part + 2 * part) = ml;
+    }
+  }
+}
+
 // One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B).
 // Optional fused steps:
 //   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
@@ -370,47 +467,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
     index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
 
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
-  int chunk;
-  const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
-                            &chunk);
+  SplitCtx sc;
+  if (!split_setup<T, D, G, 64 * kWaves>(a, b, kvh, s, sc)) return;
   const int qh0 = kvh * G;
-  if (s >= S) {
-    // a padded request (L = 0) has no split: its rows are zero
-    if (S == 0 && s == 0 && a.out)
-      for (int i = tid; i < G * D; i += 64 * kWaves)
-        store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0) * D + i, 0.f);
-    return;
-  }
-  const int lo = s * chunk;
-  const int hi = min(L, lo + chunk);
   // this wave's contiguous share of the split, a multiple of 16 tokens
-  const int sub = ceil_div(ceil_div(hi - lo, kWaves), 16) * 16;
-  const int wlo = min(hi, lo + wave * sub);
-  const int whi = min(hi, wlo + sub);
+  const int sub = ceil_div(ceil_div(sc.hi - sc.lo, kWaves), 16) * 16;
+  const int wlo = min(sc.hi, sc.lo + wave * sub);
+  const int whi = min(sc.hi, wlo + sub);
+  const int32_t* row = sc.row;
+  const int n_slots = sc.n_slots;
+  const int64_t row_stride = sc.row_stride;
 
-  const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
-  const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
-  const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
-  const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
-
-  // fused store of the new token (position L-1) by the wave that reads it
-  if (a.k_new && L - 1 >= wlo && L - 1 < whi) {
-    const int raw = row[L - 1];
-    constexpr int CPR = Gm::ROW / 16;  // 16-byte chunks of one (slot, KV head) row
-    if (raw >= 0 && raw < n_slots && lane < 2 * CPR) {
-      const int chk = lane % CPR;
-      const char* src = (const char*)(lane < CPR ? a.k_new : a.v_new) +
-                        ((int64_t)b * a.n_kv_heads + kvh) * Gm::ROW + 16 * chk;
-      char* dst = (char*)(lane < CPR ? a.k : a.v) + (int64_t)raw * row_stride +
-                  (int64_t)kvh * Gm::ROW + 16 * chk;
-      *(u32x4*)dst = *(const u32x4*)src;
-    }
-    // the row is read back below by this same wave: complete the stores first
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-  }
+  store_new_token<T, D>(a, sc, b, kvh, wlo, whi, lane);
 
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW + 16 * c;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW + 16 * c;
@@ -492,38 +560,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   }
   __syncthreads();
 
-  // Merge the waves (fixed order). A request with a single split is finished
-  // here when an output is given; otherwise the split's partial is written.
-  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits;
-  const bool direct = a.out != nullptr && S == 1;
-  for (int i = tid; i < G * D; i += 64 * kWaves) {
-    const int h = i / D;
-    const int d = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][h][0]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = red_ml[w][h][0];
-      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      num = fmaf(f, red_acc[w][h][d], num);
-      den = fmaf(f, red_ml[w][h][1], den);
-    }
-    const float o = num / den;
-    if (direct) {
-      store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0 + h) * D + d, o);
-      continue;
-    }
-    const int64_t part = part0 + (int64_t)h * a.split.max_splits + s;
-    a.o_part[part * D + d] = o;
-    if (d == 0) {
-      float2 ml;
-      ml.x = M * kLn2;
-      ml.y = den;
-      *(float2*)(a.ml_part + 2 * part) = ml;
-    }
-  }
+  finish_split<T, D, G, kWaves>(a, red_acc, red_ml, b, kvh, s, sc.S);
 }
 
 // One wave per (request, q head). Splits are taken 32 at a time: all 32
@@ -596,7 +633,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, acc[e] * inv);
 }
 
-template <typename T, int D>
+// Group sizes above MAXG are served by another kernel (the bf16 MFMA one) and
+// are not instantiated here.
+template <typename T, int D, int MAXG = 16>
 hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
@@ -604,8 +643,20 @@ hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
     case 1: decode_partial_kernel<T, D, 1><<<grid, 64 * kWaves, 0, stream>>>(a); break;
     case 2: decode_partial_kernel<T, D, 2><<<grid, 64 * kWaves, 0, stream>>>(a); break;
     case 4: decode_partial_kernel<T, D, 4><<<grid, 64 * kWaves, 0, stream>>>(a); break;
-    case 8: decode_partial_kernel<T, D, 8><<<grid, 64 * kWaves, 0, stream>>>(a); break;
-    case 16: decode_partial_kernel<T, D, 16><<<grid, 64 * kWaves, 0, stream>>>(a); break;
+    case 8:
+      if constexpr (MAXG >= 8) {
+        decode_partial_kernel<T, D, 8><<<grid, 64 * kWaves, 0, stream>>>(a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
+    case 16:
+      if constexpr (MAXG >= 16) {
+        decode_partial_kernel<T, D, 16><<<grid, 64 * kWaves, 0, stream>>>(a);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

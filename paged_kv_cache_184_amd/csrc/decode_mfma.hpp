@@ -1,0 +1,322 @@
+// Split-KV paged decode on bf16 MFMA for large query groups (a3), the
+// companion of the VALU kernel in decode_impl.hpp. Same grid, fused steps,
+// partial layout and merge; only the per-wave inner loop differs.
+//
+// With g >= 8 query heads per KV head, the VALU kernel spends most of its
+// instructions on per-head dot products and lane reductions. Here the g heads
+// of a KV head are the 16 columns of an MFMA tile (unused columns hold zero
+// queries), so per 32-key block a wave issues 2*D/32 MFMAs for S^T = K Q^T,
+// D/16 for O^T += V^T P^T and one for the row sums, and its VALU work is 8
+// softmax values per lane.
+//   * K goes from global memory straight into the MFMA A operand (lane l loads
+//     16 bytes of key l%16's row at byte 16*(l/16) + 64*ks), through a ring of
+//     three register blocks.
+//   * V is gathered into LDS by direct-to-LDS transfers (global_load_lds
+//     dwordx4, rows XOR-swizzled) in a ring of three stages per wave, and read
+//     back transposed with ds_read_b64_tr_b16 as the A operand of O^T; P^T
+//     comes straight out of the S^T accumulator layout as the B operand.
+//   * Each block's loads are issued two blocks ahead of its use in straight-
+//     line code per 128-key super-block, so every wait count is static.
+//   * Online softmax in base 2 per head (lane column), with the same lazy
+//     stabiliser as the VALU kernel; P is rounded to bf16 and the row sums are
+//     those rounded values summed by one more MFMA (a ones operand times P^T).
+#pragma once
+
+#include "decode_impl.hpp"
+
+namespace pkv {
+namespace decode_mfma {
+
+using decode_impl::finish_split;
+using decode_impl::index_step_block;
+using decode_impl::kLog2e;
+using decode_impl::kTau;
+using decode_impl::split_setup;
+using decode_impl::SplitCtx;
+using decode_impl::store_new_token;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kW = 4;      // waves per workgroup
+constexpr int kBlk = 32;   // keys per block: two 16-key MFMA tiles
+constexpr int kSB = 4;     // blocks per super-block (slot ids staged per super-block)
+constexpr int kRing = 3;   // blocks in flight per wave
+constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 1.0 in both halves
+
+#define PKV_DM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define PKV_DM_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
+
+template <int D>
+struct MGeo {
+  static constexpr int ROW = D * 2;     // bytes of one (slot, KV head) row
+  static constexpr int CPR = ROW / 16;  // 16-byte chunks per row
+  static constexpr int KS = D / 32;     // MFMA k-steps over head_dim
+  static constexpr int DT = D / 16;     // 16-row tiles of O^T over head_dim
+  static constexpr int RPI = 64 / CPR;  // V rows per wave-wide 1 KiB transfer
+  static constexpr int NI = kBlk / RPI; // V transfers per block
+  static constexpr int VST = kBlk * ROW;  // bytes of one V stage
+};
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Byte offset of logical 16-byte chunk c of row r in a swizzled V stage.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * MGeo<D>::ROW + 16 * (c ^ (r & (MGeo<D>::CPR - 1)));
+}
+
+__device__ __forceinline__ u32x2 tr_read(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <int D>
+struct KBlock {
+  u32x4 f[2][MGeo<D>::KS];  // [key tile][k-step]
+};
+
+template <int D>
+struct WaveState {
+  f32x4 o[MGeo<D>::DT];  // O^T: lane l holds d = 16 dt + 4 (l/16) + r of head l%16
+  f32x4 lsum;            // row sums (every element of the lane's column)
+  float m;               // stabiliser of head l%16, log2 units
+};
+
+// Loads of block i of a super-block: K fragments into registers, V rows into
+// the V stage by direct-to-LDS transfers. Positions past ce re-read the last
+// valid token.
+template <int D>
+__device__ __forceinline__ void issue_block(KBlock<D>& kb, char* vstage, const int* slots, int i,
+                                            int cb, int ce, const char* kbase, const char* vbase,
+                                            int64_t row_stride, int lane) {
+  using Gm = MGeo<D>;
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const int last = ce - cb - 1;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int64_t off = (int64_t)slots[min(kBlk * i + 16 * kt + col, last)] * row_stride;
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks)
+      kb.f[kt][ks] = *(const u32x4*)(kbase + off + 16 * quad + 64 * ks);
+  }
+  const int prow = lane / Gm::CPR;
+  const int pch = lane % Gm::CPR;
+#pragma unroll
+  for (int t = 0; t < Gm::NI; ++t) {
+    const int r = Gm::RPI * t + prow;  // row of the stage this lane fills
+    const int lch = pch ^ (r & (Gm::CPR - 1));
+    const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
+    __builtin_amdgcn_global_load_lds(PKV_DM_GLB(vbase + off + 16 * lch),
+                                     PKV_DM_LDS(vstage + Gm::RPI * t * Gm::ROW), 16, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>& kb,
+                                              const char* vstage, const u32x4 (&qf)[MGeo<D>::KS],
+                                              float scale2, int key0, int whi, int lane) {
+  using Gm = MGeo<D>;
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  // S^T: keys 16 kt + 4 quad + r, head col
+  f32x4 s[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Gm::KS; ++ks) s[kt] = mfma16(kb.f[kt][ks], qf[ks], s[kt]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = key0 + 16 * kt + 4 * quad + r < whi ? s[kt][r] * scale2 : -INFINITY;
+      s[kt][r] = x;
+      mx = fmaxf(mx, x);
+    }
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau) != 0) {
+    float x = fmaxf(mx, __shfl_xor(mx, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    const float mnew = fmaxf(st.m, x);
+    const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
+    st.lsum *= corr;
+#pragma unroll
+    for (int dt = 0; dt < Gm::DT; ++dt) st.o[dt] *= corr;
+    st.m = mnew;
+  }
+  // P^T in the B-operand layout: slots 0..3 = key tile 0, 4..7 = key tile 1
+  const float mm = st.m == -INFINITY ? 0.f : st.m;
+  uint32_t w[4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+      const bf16x2_t pb = {(__bf16)__builtin_amdgcn_exp2f(s[kt][r] - mm),
+                           (__bf16)__builtin_amdgcn_exp2f(s[kt][r + 1] - mm)};
+      w[2 * kt + r / 2] = __builtin_bit_cast(uint32_t, pb);
+    }
+  const u32x4 pf = u32x4{w[0], w[1], w[2], w[3]};
+  st.lsum = mfma16(u32x4{kOnes, kOnes, kOnes, kOnes}, pf, st.lsum);
+  // O^T += V^T P^T. ds_read_b64_tr_b16 hands lane i of each 16-lane group
+  // element i%4 of the 8-byte segments of lanes i/4, i/4+4, i/4+8, i/4+12;
+  // pointing those at keys 4 quad + (0..3) (+16) and columns 16 dt + 4 (col%4)
+  // gives every lane its column's values in the key order of P^T.
+  const int s4 = col & 3;
+  const int r0 = 4 * quad + (col >> 2);
+#pragma unroll
+  for (int dt = 0; dt < Gm::DT; ++dt) {
+    const int chunk = 2 * dt + (s4 >> 1);
+    const int half = 8 * (s4 & 1);
+    const u32x2 lo = tr_read(vstage + swz<D>(r0, chunk) + half);
+    const u32x2 hi = tr_read(vstage + swz<D>(r0 + 16, chunk) + half);
+    st.o[dt] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, st.o[dt]);
+  }
+}
+
+// NB consecutive 32-key blocks of one super-block, straight-line: block i's
+// loads are issued two blocks before its compute, into ring entry i % 3.
+template <int D, int NB>
+__device__ __forceinline__ void block_run(WaveState<D>& st, char* vs0, char* vs1, char* vs2,
+                                          const int* slots, int cb, int ce,
+                                          const u32x4 (&qf)[MGeo<D>::KS], const char* kbase,
+                                          const char* vbase, int64_t row_stride, float scale2,
+                                          int whi, int lane) {
+  KBlock<D> kb[kRing];
+  auto stage = [&](int i) -> char* { return i % 3 == 0 ? vs0 : (i % 3 == 1 ? vs1 : vs2); };
+  issue_block<D>(kb[0], stage(0), slots, 0, cb, ce, kbase, vbase, row_stride, lane);
+  if (NB > 1) issue_block<D>(kb[1], stage(1), slots, 1, cb, ce, kbase, vbase, row_stride, lane);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    if (i + 2 < NB)
+      issue_block<D>(kb[(i + 2) % 3], stage(i + 2), slots, i + 2, cb, ce, kbase, vbase,
+                     row_stride, lane);
+    compute_block<D>(st, kb[i % 3], stage(i), qf, scale2, cb + kBlk * i, whi, lane);
+  }
+  // every lane's transpose reads of this super-block precede the next one's
+  // transfers into the same stages
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeArgs a) {
+  using Gm = MGeo<D>;
+  static_assert(G <= 16, "one MFMA column per query head");
+  __shared__ __attribute__((aligned(1024))) char vs0[kW][Gm::VST];
+  __shared__ __attribute__((aligned(1024))) char vs1[kW][Gm::VST];
+  __shared__ __attribute__((aligned(1024))) char vs2[kW][Gm::VST];
+  __shared__ int slot_lds[kW][kSB * kBlk];
+  __shared__ float red_acc[kW][G][D];
+  __shared__ float red_ml[kW][G][2];
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const int kvh = blockIdx.x;  // KV head fastest: XCD-balanced (see decode_impl.hpp)
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+
+  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
+    index_step_block<64 * kW>(a, &slot_lds[0][0]);
+
+  SplitCtx sc;
+  if (!split_setup<bf16_t, D, G, 64 * kW>(a, b, kvh, s, sc)) return;
+  // this wave's contiguous share of the split, a multiple of 32 tokens
+  const int sub = ceil_div(ceil_div(sc.hi - sc.lo, kW), kBlk) * kBlk;
+  const int wlo = min(sc.hi, sc.lo + wave * sub);
+  const int whi = min(sc.hi, wlo + sub);
+  store_new_token<bf16_t, D>(a, sc, b, kvh, wlo, whi, lane);
+
+  const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
+  const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
+  constexpr int SBK = kSB * kBlk;  // keys per super-block
+  int ids[SBK / 64];
+  if (wlo < whi) {
+#pragma unroll
+    for (int j = 0; j < SBK / 64; ++j) ids[j] = sc.row[min(wlo + lane + 64 * j, whi - 1)];
+  }
+  // Q^T fragments (B operand): head col, head_dim 8 quad + 32 ks .. +7; zero
+  // for the columns past the group
+  const int qh0 = kvh * G;
+  u32x4 qf[Gm::KS];
+  const char* qp = (const char*)a.q + ((int64_t)b * a.n_q_heads + qh0 + min(col, G - 1)) * Gm::ROW +
+                   16 * quad;
+#pragma unroll
+  for (int ks = 0; ks < Gm::KS; ++ks) {
+    const u32x4 v = *(const u32x4*)(qp + 64 * ks);
+    qf[ks] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+  const float scale2 = a.scale * kLog2e;
+  WaveState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < Gm::DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.lsum = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+
+  int* slots = slot_lds[wave];
+  char* v0 = vs0[wave];
+  char* v1 = vs1[wave];
+  char* v2 = vs2[wave];
+  for (int cb = wlo; cb < whi; cb += SBK) {
+    const int ce = min(whi, cb + SBK);
+#pragma unroll
+    for (int j = 0; j < SBK / 64; ++j) slots[lane + 64 * j] = clamp_index(ids[j], sc.n_slots);
+    // other lanes of this wave read these ids: order the LDS writes first
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int nb = cb + SBK;
+    if (nb < whi) {
+#pragma unroll
+      for (int j = 0; j < SBK / 64; ++j) ids[j] = sc.row[min(nb + lane + 64 * j, whi - 1)];
+    }
+    switch (ceil_div(ce - cb, kBlk)) {
+#define PKV_DM_RUN(n)                                                                         \
+  case n:                                                                                     \
+    block_run<D, n>(st, v0, v1, v2, slots, cb, ce, qf, kbase, vbase, sc.row_stride, scale2,   \
+                    whi, lane);                                                               \
+    break;
+      PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
+#undef PKV_DM_RUN
+      default: break;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
+  }
+
+  // Hand the wave's (m, l, O) to LDS; an empty wave leaves m = -inf, l = 0, O = 0.
+  if (col < G) {
+#pragma unroll
+    for (int dt = 0; dt < Gm::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_acc[wave][col][16 * dt + 4 * quad + r] = st.o[dt][r];
+    if (quad == 0) {
+      red_ml[wave][col][0] = st.m;
+      red_ml[wave][col][1] = st.lsum[0];
+    }
+  }
+  __syncthreads();
+  finish_split<bf16_t, D, G, kW>(a, red_acc, red_ml, b, kvh, s, sc.S);
+}
+
+template <int D>
+hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
+  const int g = a.n_q_heads / a.n_kv_heads;
+  dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
+  switch (g) {
+    case 8: decode_mfma_kernel<D, 8><<<grid, 64 * kW, 0, stream>>>(a); break;
+    case 16: decode_mfma_kernel<D, 16><<<grid, 64 * kW, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace decode_mfma
+}  // namespace pkv

@@ -126,10 +126,11 @@ def test_group_and_dims(g, d, dtype):
     full_check(b, 41, [ops.split_cfg(8, 0, 64)], layer=1)
 
 
-def test_slot_relocation_bit_exact():
+@pytest.mark.parametrize("hq", [16, 32])  # g = 4 (VALU kernel), g = 8 (MFMA kernel)
+def test_slot_relocation_bit_exact(hq):
     """Moving every live row to another slot (and remapping the table) gives
     bit-identical output: the reduction order depends on token position only."""
-    b = W.custom("reloc", n_layers=1, n_slots=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+    b = W.custom("reloc", n_layers=1, n_slots=2048, n_q_heads=hq, n_kv_heads=4, head_dim=128,
                  dtype="bf16", seq_lens=[300, 1, 999], n_new=[1, 1, 1], seed=50)
     vals = W.host_values(b, 51)
     db = DeviceBatch(b, vals)
@@ -156,16 +157,17 @@ def test_determinism():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_length_one_is_v_exactly():
-    b = W.custom("len1", n_layers=1, n_slots=256, n_q_heads=8, n_kv_heads=2, head_dim=128,
+@pytest.mark.parametrize("g,d", [(4, 128), (8, 128), (16, 64)])
+def test_length_one_is_v_exactly(g, d):
+    b = W.custom("len1", n_layers=1, n_slots=256, n_q_heads=2 * g, n_kv_heads=2, head_dim=d,
                  dtype="bf16", seq_lens=[1, 1, 1], n_new=[1, 1, 1], seed=70)
     vals = W.host_values(b, 71)
     db = DeviceBatch(b, vals)
     out, _ = run_decode(db, 0, ops.split_cfg(4, 0, 16))
     for i in range(3):
         slot = b.req_to_token[b.req_pool_indices[i], 0]
-        for h in range(8):
-            assert torch.equal(out[i, h].view(torch.int16), db.v_pool[0, slot, h // 4].view(torch.int16))
+        for h in range(2 * g):
+            assert torch.equal(out[i, h].view(torch.int16), db.v_pool[0, slot, h // g].view(torch.int16))
 
 
 def test_equal_keys_mean_of_v():
@@ -255,10 +257,13 @@ def test_error_leaves_output_untouched():
     assert torch.all(out == 7.0)
 
 
-def test_decode_step_fused_matches_separate_calls():
+@pytest.mark.parametrize("hq", [32, 64])  # g = 4 (VALU kernel), g = 8 (MFMA kernel)
+def test_decode_step_fused_matches_separate_calls(hq):
     """pkv_decode_step (index step + store + attention in one launch) against the
     separate calls: index outputs and the stored pool bit-exact, output identical."""
     b = W.ragged_decode(8)
+    if hq != b.n_q_heads:
+        b = dataclasses.replace(b, n_q_heads=hq)
     vals = W.host_values(b, 140)
     split = split_for(b, tokens=256)
     # separate calls
