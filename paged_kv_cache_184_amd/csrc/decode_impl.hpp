@@ -394,11 +394,12 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const Split
 
 // Merge the W waves' (m, l, acc) from LDS (fixed order) into the split's
 // normalised output: written directly for a single-split request when an
-// output is given, else as the split's partial (o, (m ln2, l)).
+// output is given, else as the split's partial (o, (m ln2, l)). Wave w's
+// accumulator rows are red_acc[w * wstride + h * D + d].
 template <typename T, int D, int G, int W>
-__device__ __forceinline__ void finish_split(const DecodeArgs& a, const float (*red_acc)[G][D],
-                                             const float (*red_ml)[G][2], int b, int kvh, int s,
-                                             int S) {
+__device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* red_acc,
+                                             int wstride, const float (*red_ml)[G][2], int b,
+                                             int kvh, int s, int S) {
   const int qh0 = kvh * G;
   const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits;
   const bool direct = a.out != nullptr && S == 1;
@@ -413,7 +414,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float (*
     for (int w = 0; w < W; ++w) {
       const float mw = red_ml[w][h][0];
       const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      num = fmaf(f, red_acc[w][h][d], num);
+      num = fmaf(f, red_acc[w * wstride + h * D + d], num);
       den = fmaf(f, red_ml[w][h][1], den);
     }
     const float o = num / den;
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   }
   __syncthreads();
 
-  finish_split<T, D, G, kWaves>(a, red_acc, red_ml, b, kvh, s, sc.S);
+  finish_split<T, D, G, kWaves>(a, &red_acc[0][0][0], G * D, red_ml, b, kvh, s, sc.S);
 }
 
 // One wave per (request, q head). Splits are taken 32 at a time: all 32

@@ -9,14 +9,20 @@
 // D/16 for O^T += V^T P^T and one for the row sums, and its VALU work is 8
 // softmax values per lane.
 //   * K goes from global memory straight into the MFMA A operand (lane l loads
-//     16 bytes of key l%16's row at byte 16*(l/16) + 64*ks), through a ring of
-//     three register blocks.
-//   * V is gathered into LDS by direct-to-LDS transfers (global_load_lds
-//     dwordx4, rows XOR-swizzled) in a ring of three stages per wave, and read
-//     back transposed with ds_read_b64_tr_b16 as the A operand of O^T; P^T
-//     comes straight out of the S^T accumulator layout as the B operand.
-//   * Each block's loads are issued two blocks ahead of its use in straight-
+//     16 bytes of key l%16's row at byte 16*(l/16) + 64*ks); K and V of a
+//     block are a ring of two register blocks.
+//   * V rows are loaded into registers in the layout of a wave-wide 1 KiB
+//     LDS transfer, written to a per-wave LDS tile (rows XOR-swizzled) when
+//     their block is computed, and read back transposed with
+//     ds_read_b64_tr_b16 as the A operand of O^T; P^T comes straight out of
+//     the S^T accumulator layout as the B operand. (Direct-to-LDS loads would
+//     save the registers, but with them in flight the compiler waits for all
+//     outstanding loads before any register load is used.)
+//   * Each block's loads are issued one block ahead of its use in straight-
 //     line code per 128-key super-block, so every wait count is static.
+//   * 8 KiB of LDS per wave (the wave-merge buffer reuses it) and at most 256
+//     registers: two or more workgroups share a CU, so one hides the others'
+//     start-up and drain.
 //   * Online softmax in base 2 per head (lane column), with the same lazy
 //     stabiliser as the VALU kernel; P is rounded to bf16 and the row sums are
 //     those rounded values summed by one more MFMA (a ones operand times P^T).
@@ -43,11 +49,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kW = 4;      // waves per workgroup
 constexpr int kBlk = 32;   // keys per block: two 16-key MFMA tiles
 constexpr int kSB = 4;     // blocks per super-block (slot ids staged per super-block)
-constexpr int kRing = 3;   // blocks in flight per wave
+constexpr int kRing = 2;   // blocks in flight per wave (ring of K and V registers)
 constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 1.0 in both halves
 
-#define PKV_DM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-#define PKV_DM_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
 
 template <int D>
 struct MGeo {
@@ -57,7 +61,7 @@ struct MGeo {
   static constexpr int DT = D / 16;     // 16-row tiles of O^T over head_dim
   static constexpr int RPI = 64 / CPR;  // V rows per wave-wide 1 KiB transfer
   static constexpr int NI = kBlk / RPI; // V transfers per block
-  static constexpr int VST = kBlk * ROW;  // bytes of one V stage
+  static constexpr int VST = kBlk * ROW;  // bytes of one V tile
 };
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -65,7 +69,7 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Byte offset of logical 16-byte chunk c of row r in a swizzled V stage.
+// Byte offset of logical 16-byte chunk c of row r in a swizzled V tile.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   return r * MGeo<D>::ROW + 16 * (c ^ (r & (MGeo<D>::CPR - 1)));
@@ -79,7 +83,8 @@ __device__ __forceinline__ u32x2 tr_read(const char* p) {
 
 template <int D>
 struct KBlock {
-  u32x4 f[2][MGeo<D>::KS];  // [key tile][k-step]
+  u32x4 f[2][MGeo<D>::KS];  // K: [key tile][k-step]
+  u32x4 v[MGeo<D>::NI];     // V: this lane's 16 bytes of each 1 KiB row group
 };
 
 template <int D>
@@ -89,12 +94,13 @@ struct WaveState {
   float m;               // stabiliser of head l%16, log2 units
 };
 
-// Loads of block i of a super-block: K fragments into registers, V rows into
-// the V stage by direct-to-LDS transfers. Positions past ce re-read the last
-// valid token.
+// Loads of block i of a super-block into registers: K fragments, and V in
+// the layout its LDS tile is written in (lane l of row group t holds row
+// RPI t + l / CPR, physical chunk l % CPR). Positions past ce re-read the
+// last valid token.
 template <int D>
-__device__ __forceinline__ void issue_block(KBlock<D>& kb, char* vstage, const int* slots, int i,
-                                            int cb, int ce, const char* kbase, const char* vbase,
+__device__ __forceinline__ void issue_block(KBlock<D>& kb, const int* slots, int i, int cb,
+                                            int ce, const char* kbase, const char* vbase,
                                             int64_t row_stride, int lane) {
   using Gm = MGeo<D>;
   const int col = lane & 15;
@@ -111,21 +117,25 @@ __device__ __forceinline__ void issue_block(KBlock<D>& kb, char* vstage, const i
   const int pch = lane % Gm::CPR;
 #pragma unroll
   for (int t = 0; t < Gm::NI; ++t) {
-    const int r = Gm::RPI * t + prow;  // row of the stage this lane fills
+    const int r = Gm::RPI * t + prow;
     const int lch = pch ^ (r & (Gm::CPR - 1));
     const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
-    __builtin_amdgcn_global_load_lds(PKV_DM_GLB(vbase + off + 16 * lch),
-                                     PKV_DM_LDS(vstage + Gm::RPI * t * Gm::ROW), 16, 0, 0);
+    kb.v[t] = *(const u32x4*)(vbase + off + 16 * lch);
   }
 }
 
 template <int D>
 __device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>& kb,
-                                              const char* vstage, const u32x4 (&qf)[MGeo<D>::KS],
+                                              char* vstage, const u32x4 (&qf)[MGeo<D>::KS],
                                               float scale2, int key0, int whi, int lane) {
   using Gm = MGeo<D>;
   const int col = lane & 15;
   const int quad = lane >> 4;
+  // V tile into LDS first (read back transposed below, after the S MFMAs;
+  // this wave's earlier reads of the tile precede these writes in LDS order)
+#pragma unroll
+  for (int t = 0; t < Gm::NI; ++t)
+    *(u32x4*)(vstage + Gm::RPI * t * Gm::ROW + 16 * lane) = kb.v[t];
   // S^T: keys 16 kt + 4 quad + r, head col
   f32x4 s[2];
 #pragma unroll
@@ -183,39 +193,31 @@ __device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>&
 }
 
 // NB consecutive 32-key blocks of one super-block, straight-line: block i's
-// loads are issued two blocks before its compute, into ring entry i % 3.
+// loads are issued one block before its compute, into ring entry i % 2.
 template <int D, int NB>
-__device__ __forceinline__ void block_run(WaveState<D>& st, char* vs0, char* vs1, char* vs2,
-                                          const int* slots, int cb, int ce,
-                                          const u32x4 (&qf)[MGeo<D>::KS], const char* kbase,
-                                          const char* vbase, int64_t row_stride, float scale2,
-                                          int whi, int lane) {
+__device__ __forceinline__ void block_run(WaveState<D>& st, char* vstage, const int* slots,
+                                          int cb, int ce, const u32x4 (&qf)[MGeo<D>::KS],
+                                          const char* kbase, const char* vbase,
+                                          int64_t row_stride, float scale2, int whi, int lane) {
   KBlock<D> kb[kRing];
-  auto stage = [&](int i) -> char* { return i % 3 == 0 ? vs0 : (i % 3 == 1 ? vs1 : vs2); };
-  issue_block<D>(kb[0], stage(0), slots, 0, cb, ce, kbase, vbase, row_stride, lane);
-  if (NB > 1) issue_block<D>(kb[1], stage(1), slots, 1, cb, ce, kbase, vbase, row_stride, lane);
+  issue_block<D>(kb[0], slots, 0, cb, ce, kbase, vbase, row_stride, lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    if (i + 2 < NB)
-      issue_block<D>(kb[(i + 2) % 3], stage(i + 2), slots, i + 2, cb, ce, kbase, vbase,
-                     row_stride, lane);
-    compute_block<D>(st, kb[i % 3], stage(i), qf, scale2, cb + kBlk * i, whi, lane);
+    if (i + 1 < NB)
+      issue_block<D>(kb[(i + 1) % 2], slots, i + 1, cb, ce, kbase, vbase, row_stride, lane);
+    // keep the next block's loads ahead of this block's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    compute_block<D>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
   }
-  // every lane's transpose reads of this super-block precede the next one's
-  // transfers into the same stages
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
   using Gm = MGeo<D>;
   static_assert(G <= 16, "one MFMA column per query head");
+  static_assert(G * D * 4 <= Gm::VST, "a wave's merge rows fit in its V tile");
   __shared__ __attribute__((aligned(1024))) char vs0[kW][Gm::VST];
-  __shared__ __attribute__((aligned(1024))) char vs1[kW][Gm::VST];
-  __shared__ __attribute__((aligned(1024))) char vs2[kW][Gm::VST];
   __shared__ int slot_lds[kW][kSB * kBlk];
-  __shared__ float red_acc[kW][G][D];
   __shared__ float red_ml[kW][G][2];
 
   const int wave = threadIdx.x >> 6;
@@ -265,8 +267,6 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeArgs a) {
 
   int* slots = slot_lds[wave];
   char* v0 = vs0[wave];
-  char* v1 = vs1[wave];
-  char* v2 = vs2[wave];
   for (int cb = wlo; cb < whi; cb += SBK) {
     const int ce = min(whi, cb + SBK);
 #pragma unroll
@@ -281,8 +281,8 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeArgs a) {
     switch (ceil_div(ce - cb, kBlk)) {
 #define PKV_DM_RUN(n)                                                                         \
   case n:                                                                                     \
-    block_run<D, n>(st, v0, v1, v2, slots, cb, ce, qf, kbase, vbase, sc.row_stride, scale2,   \
-                    whi, lane);                                                               \
+    block_run<D, n>(st, v0, slots, cb, ce, qf, kbase, vbase, sc.row_stride, scale2, whi,      \
+                    lane);                                                                    \
     break;
       PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
 #undef PKV_DM_RUN
@@ -292,18 +292,22 @@ __global__ __launch_bounds__(64 * kW) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Hand the wave's (m, l, O) to LDS; an empty wave leaves m = -inf, l = 0, O = 0.
+  // The O rows go into this wave's V tile (its transpose reads have returned:
+  // their results fed the last MFMAs).
   if (col < G) {
+    float* mine = (float*)vs0[wave];
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red_acc[wave][col][16 * dt + 4 * quad + r] = st.o[dt][r];
+      for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[dt][r];
     if (quad == 0) {
       red_ml[wave][col][0] = st.m;
       red_ml[wave][col][1] = st.lsum[0];
     }
   }
   __syncthreads();
-  finish_split<bf16_t, D, G, kW>(a, red_acc, red_ml, b, kvh, s, sc.S);
+  finish_split<bf16_t, D, G, kW>(a, (const float*)&vs0[0][0], Gm::VST / 4, red_ml, b, kvh, s,
+                                 sc.S);
 }
 
 template <int D>
