@@ -159,6 +159,21 @@ class DecodeBench:
                 self.out, k_new=self.k_new, v_new=self.v_new, kv_indptr_out=self.kv_indptr,
                 loc_out=self.loc, splits_out=self.splits))
         self.mode = "fused"
+        # attention alone, plain or cascade (shared prefixes read once per group)
+        self.attn_only = [c[2] for c in self.calls]
+        self.cascade = None
+        shared = getattr(b, "shared_rows", None)
+        if shared is not None and len(shared) > 1:
+            P = 2048  # the ragged workload's shared prefix
+            plen = np.zeros(B, np.int32)
+            plen[shared] = P
+            t = lambda x: torch.tensor(np.asarray(x, np.int32), device=dev)
+            self.groups = ops.make_prefix_groups(t(plen), t([0, len(shared)]), t(shared),
+                                                 len(shared))
+            self.cascade = [ops.prepare_cascade_decode(self.q, self.k_pool, self.v_pool, layer,
+                                                       self.meta, self.groups, b.scale,
+                                                       self.split, self.ws, self.out)
+                            for layer in range(b.n_layers)]
 
     # algorithmic bytes
     def kv_bytes(self) -> int:
@@ -183,6 +198,10 @@ class DecodeBench:
         """One decode step for layer i mod n_layers."""
         if self.mode == "fused":
             self.fused[i % len(self.fused)]()
+            return
+        if self.mode in ("attn", "cascade"):
+            calls = self.attn_only if self.mode == "attn" else self.cascade
+            calls[i % len(calls)]()
             return
         for call in self.calls[i % len(self.calls)]:
             call()
@@ -507,6 +526,18 @@ def main():
                                              (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
                 "splits": int(db.split.max_splits), "split_tokens": int(db.split.split_tokens),
                 "max_abs_err_request0": err}
+            if db.cascade is not None:
+                # attention alone: plain decode vs cascade (the shared prefix read
+                # once per group); the split cap leaves room for prefix splits
+                db.mode = "attn"
+                attn_ms, _ = db.run(steps, 2)
+                db.mode = "cascade"
+                casc_ms, _ = db.run(steps, 2)
+                detail[name].update({
+                    "attn_us": round(attn_ms * 1e3, 2), "cascade_attn_us": round(casc_ms * 1e3, 2),
+                    "cascade_kv_gbs_unique": round(db.kv_bytes_unique() / (casc_ms * 1e-3) / 1e9,
+                                                   1),
+                    "shared_group": len(db.b.shared_rows)})
             print(f"# {name}: {detail[name]}", file=sys.stderr, flush=True)
             del db
             torch.cuda.empty_cache()

@@ -234,6 +234,48 @@ pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q
                            int32_t* kv_indptr_out, int32_t* loc_out, int32_t* splits_out,
                            void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
+/* ---- cascade (shared-prefix) decode --------------------------------------
+ * Requests of a prefix group map their first P positions to the same slots
+ * (P1, bullets on rebuilding request mappings for cached prefix pages and on
+ * prefix-reuse regressions; P4, bullet on packing prompts with a shared
+ * prefix start). The result is that of pkv_paged_decode_attn for the same
+ * requests; the difference is that each group's prefix K/V is read once per
+ * 16 / g members (g = n_q_heads / n_kv_heads): their query heads are the 16
+ * columns of one MFMA tile. Prefix and private-suffix work run in one launch.
+ *   prefix_len:   device int32 [batch], shared-prefix length P_b of request b
+ *                 (0: none; clamped to [0, L_b]); every member of a group must
+ *                 have the group's P, and its first P table entries must equal
+ *                 those of the group's first member, whose entries are read.
+ *                 A member whose P differs from the first member's gets no
+ *                 prefix partials: its output is unspecified (memory-safe).
+ *   group_indptr: device int32 [n_groups + 1], members: device int32 request
+ *                 indices [n_members]; group i is members[group_indptr[i] ..
+ *                 group_indptr[i+1]-1], a request in at most one group
+ *                 (positions are clamped to [0, n_members)).
+ *   max_members:  host bound on the size of every group, in [1, 65535] (extra
+ *                 members are ignored); the launch has n_groups *
+ *                 ceil(max_members / (16 / g)) prefix rows besides the batch,
+ *                 at most 65535 in all (PKV_EINVAL otherwise). */
+typedef struct pkv_prefix_groups {
+  const int32_t* prefix_len;
+  const int32_t* group_indptr;
+  const int32_t* members;
+  int32_t n_groups;
+  int32_t max_members;
+  int32_t n_members;
+  int32_t reserved;
+} pkv_prefix_groups;
+
+/* Split plan: the prefix of a request forms splits under a cap of
+ * max_splits / 2 (partial indices first), its private suffix of L_b - P_b keys
+ * splits under the rest of the cap (after them); max_splits >= 2; BF16 pools
+ * only. The workspace is sized as for pkv_paged_decode_attn. */
+pkv_status pkv_cascade_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                   int32_t n_q_heads, const pkv_batch_meta* meta,
+                                   const pkv_prefix_groups* groups, float scale,
+                                   pkv_split_cfg split, void* workspace, size_t ws_bytes,
+                                   void* out, hipStream_t stream);
+
 /* a3 alone: writes the split partials of pkv_paged_decode_attn into the workspace
  * (no merge). */
 pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const void* q,

@@ -29,7 +29,7 @@ EXPORTS = (
     "pkv_abi_version", "pkv_status_str", "pkv_last_error", "pkv_kv_store", "pkv_rope_kv_store",
     "pkv_build_metadata",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attn",
-    "pkv_decode_step", "pkv_decode_partials",
+    "pkv_decode_step", "pkv_cascade_decode_attn", "pkv_decode_partials",
     "pkv_decode_merge", "pkv_paged_prefill_attn", "pkv_validate_meta",
 )
 
@@ -45,6 +45,12 @@ class BatchMeta(C.Structure):
                 ("n_req_rows", C.c_int32), ("batch", C.c_int32),
                 ("req_pool_indices", C.c_void_p), ("seq_lens", C.c_void_p),
                 ("qo_indptr", C.c_void_p), ("kv_indptr", C.c_void_p)]
+
+
+class PrefixGroups(C.Structure):
+    _fields_ = [("prefix_len", C.c_void_p), ("group_indptr", C.c_void_p),
+                ("members", C.c_void_p), ("n_groups", C.c_int32), ("max_members", C.c_int32),
+                ("n_members", C.c_int32), ("reserved", C.c_int32)]
 
 
 class SplitCfg(C.Structure):
@@ -71,6 +77,7 @@ def load(path: str = LIB_PATH):
     lib = C.CDLL(path)
     P, I32, I64, F32, SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
     pool_p, meta_p = C.POINTER(KVPool), C.POINTER(BatchMeta)
+    groups_p = C.POINTER(PrefixGroups)
     sig = {
         "pkv_abi_version": (C.c_int, []),
         "pkv_status_str": (C.c_char_p, [I32]),
@@ -82,6 +89,8 @@ def load(path: str = LIB_PATH):
         "pkv_decode_step": (I32, [pool_p, I32, P, P, P, I32, meta_p, F32, SplitCfg, P, P, P, P, SZ,
                                   P, P]),
         "pkv_paged_decode_attn": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P, P]),
+        "pkv_cascade_decode_attn": (I32, [pool_p, I32, P, I32, meta_p, groups_p, F32, SplitCfg, P,
+                                          SZ, P, P]),
         "pkv_decode_partials": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P]),
         "pkv_decode_merge": (I32, [meta_p, I32, I32, I32, SplitCfg, P, SZ, P, P]),
         "pkv_paged_prefill_attn": (I32, [pool_p, I32, P, I32, meta_p, I32, I32, F32, I32, P, P]),

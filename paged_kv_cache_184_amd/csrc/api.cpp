@@ -167,6 +167,12 @@ pkv_status decode_prepare(const pkv_kv_pool* pool, int32_t layer, const void* q,
   a->kv_indptr_out = nullptr;
   a->loc_out = nullptr;
   a->splits_out = nullptr;
+  a->prefix_len = nullptr;
+  a->group_indptr = nullptr;
+  a->group_members = nullptr;
+  a->n_groups = 0;
+  a->max_members = 0;
+  a->n_members = 0;
   return PKV_OK;
 }
 
@@ -284,7 +290,7 @@ pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const voi
                                int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
                                pkv_split_cfg split, void* workspace, size_t ws_bytes,
                                hipStream_t stream) {
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
   if (s != PKV_OK) return s;
   return hip_status(pkv::launch_decode_partials(a, stream), "decode partial launch");
@@ -329,7 +335,7 @@ pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const v
                                  int32_t n_q_heads, const pkv_batch_meta* meta, float scale,
                                  pkv_split_cfg split, void* workspace, size_t ws_bytes,
                                  void* out, hipStream_t stream) {
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
   if (s != PKV_OK) return s;
   if (meta->batch == 0) return ok();
@@ -342,12 +348,58 @@ pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const v
   return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
 }
 
+pkv_status pkv_cascade_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                   int32_t n_q_heads, const pkv_batch_meta* meta,
+                                   const pkv_prefix_groups* groups, float scale,
+                                   pkv_split_cfg split, void* workspace, size_t ws_bytes,
+                                   void* out, hipStream_t stream) {
+  pkv::DecodeArgs a{};
+  pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
+  if (s != PKV_OK) return s;
+  if (!groups) return fail(PKV_EINVAL, "groups is NULL");
+  if (pool->dtype != PKV_BF16)
+    return fail(PKV_EUNSUPPORTED, "cascade decode supports BF16 only (MFMA prefix kernel)");
+  if (split.max_splits < 2) return fail(PKV_EINVAL, "cascade decode needs max_splits >= 2");
+  if (groups->n_groups < 0 || groups->n_groups > kMaxBatch)
+    return fail(PKV_EINVAL, "n_groups %d outside [0, %d]", groups->n_groups, kMaxBatch);
+  const int g = n_q_heads / pool->n_kv_heads;
+  if (groups->n_groups > 0) {
+    if (!groups->prefix_len || !groups->group_indptr || !groups->members)
+      return fail(PKV_EINVAL, "prefix_len, group_indptr and members are required");
+    if (groups->max_members < 1 || groups->max_members > kMaxBatch)
+      return fail(PKV_EINVAL, "max_members %d outside [1, %d]", groups->max_members, kMaxBatch);
+    if (groups->n_members < 1) return fail(PKV_EINVAL, "n_members must be >= 1");
+    const int64_t z = (int64_t)groups->n_groups *
+                          pkv::cascade_tiles(n_q_heads, pool->n_kv_heads, groups->max_members) +
+                      meta->batch;
+    if (z > kMaxBatch)
+      return fail(PKV_EINVAL, "n_groups x ceil(max_members / (16 / %d)) + batch = %lld > %d", g,
+                  (long long)z, kMaxBatch);
+  }
+  if (meta->batch == 0) return ok();
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  if (!aligned16(out)) return fail(PKV_EALIGN, "out must be 16-byte aligned");
+  a.out = out;
+  a.merge_multi_only = true;
+  if (groups->n_groups > 0) {
+    a.prefix_len = groups->prefix_len;
+    a.group_indptr = groups->group_indptr;
+    a.group_members = groups->members;
+    a.n_groups = groups->n_groups;
+    a.max_members = groups->max_members;
+    a.n_members = groups->n_members;
+  }
+  hipError_t e = pkv::launch_cascade_partials(a, stream);
+  if (e != hipSuccess) return hip_status(e, "cascade partial launch");
+  return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
+}
+
 pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q,
                            const void* k_new, const void* v_new, int32_t n_q_heads,
                            const pkv_batch_meta* meta, float scale, pkv_split_cfg split,
                            int32_t* kv_indptr_out, int32_t* loc_out, int32_t* splits_out,
                            void* workspace, size_t ws_bytes, void* out, hipStream_t stream) {
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
   if (s != PKV_OK) return s;
   if ((k_new == nullptr) != (v_new == nullptr))

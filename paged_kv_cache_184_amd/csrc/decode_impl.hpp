@@ -335,34 +335,69 @@ __device__ void index_step_block(const DecodeArgs& a, int* scan_lds) {
   __syncthreads();
 }
 
+// Split plan of request b. Without a shared prefix its L keys form S splits
+// (the split rule of pkv_split_cfg). With a shared prefix of P > 0 keys
+// (cascade decode), the prefix forms Sp splits under a cap of max_splits / 2
+// (computed once per prefix group by the prefix kernel, partial indices
+// [0, Sp)) and the private suffix of L - P keys forms S splits under the rest
+// of the cap (partial indices [Sp, Sp + S)).
+struct Plan {
+  int L, P;     // keys, shared-prefix keys
+  int Sp;       // prefix splits
+  int S, chunk; // suffix splits and their length
+};
+
+__host__ __device__ __forceinline__ int prefix_cap(int max_splits) { return max_splits / 2; }
+
+__device__ __forceinline__ Plan plan_for(const DecodeArgs& a, int b) {
+  Plan p;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+  p.L = L;
+  int P = a.prefix_len ? a.prefix_len[b] : 0;
+  P = P < 0 ? 0 : (P > L ? L : P);
+  p.P = P;
+  int cap = a.split.max_splits;
+  p.Sp = 0;
+  if (P > 0) {
+    int chunk_p;
+    p.Sp = split_count(P, prefix_cap(cap), a.split.fixed_splits, a.split.split_tokens, &chunk_p);
+    cap -= prefix_cap(cap);
+  }
+  p.S = split_count(L - P, cap, a.split.fixed_splits, a.split.split_tokens, &p.chunk);
+  return p;
+}
+
 // What a split workgroup needs to know about its request and token range.
 struct SplitCtx {
   int L, S, chunk, lo, hi;
+  int Sp;               // partial index of this request's first suffix split
   int64_t row_stride;   // bytes between consecutive slots of one pool layer
   const int32_t* row;   // req_to_token row of the request
   int n_slots;
 };
 
-// Request length, split plan and this split's token range. Returns false when
-// the workgroup has no split to compute (after zeroing a padded request's
-// output rows when an output is given).
+// Request length, split plan and this (suffix) split's token range. Returns
+// false when the workgroup has no split to compute (after zeroing a padded
+// request's output rows when an output is given).
 template <typename T, int D, int G, int NT>
 __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh, int s,
                                             SplitCtx& c) {
   constexpr int ROW = D * elem_size<T>::value;
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
-  c.L = L;
-  c.S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens, &c.chunk);
+  const Plan p = plan_for(a, b);
+  c.L = p.L;
+  c.S = p.S;
+  c.Sp = p.Sp;
+  c.chunk = p.chunk;
   if (s >= c.S) {
     // a padded request (L = 0) has no split: its rows are zero
-    if (c.S == 0 && s == 0 && a.out)
+    if (c.S == 0 && c.Sp == 0 && s == 0 && a.out)
       for (int i = threadIdx.x; i < G * D; i += NT)
         store_out<T>(a.out, ((int64_t)b * a.n_q_heads + kvh * G) * D + i, 0.f);
     return false;
   }
-  c.lo = s * c.chunk;
-  c.hi = min(L, c.lo + c.chunk);
+  c.lo = p.P + s * c.chunk;
+  c.hi = min(c.L, c.lo + c.chunk);
   const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
   c.row = a.req_to_token + (int64_t)r * a.stride;
   c.n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
@@ -399,10 +434,10 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const Split
 template <typename T, int D, int G, int W>
 __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* red_acc,
                                              int wstride, const float (*red_ml)[G][2], int b,
-                                             int kvh, int s, int S) {
+                                             int kvh, int s, const SplitCtx& c) {
   const int qh0 = kvh * G;
-  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits;
-  const bool direct = a.out != nullptr && S == 1;
+  const int64_t part0 = ((int64_t)b * a.n_q_heads + qh0) * a.split.max_splits + c.Sp;
+  const bool direct = a.out != nullptr && c.Sp + c.S == 1;
   for (int i = threadIdx.x; i < G * D; i += 64 * W) {
     const int h = i / D;
     const int d = i % D;
@@ -433,40 +468,23 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* r
   }
 }
 
-// One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B).
-// Optional fused steps:
-//   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
-//     index step for the whole batch;
-//   a.k_new / v_new: the wave whose share holds position L-1 first stores the
-//     new token's K/V row of this KV head at slot req_to_token[r_b, L-1]
-//     (skipped if that slot is out of range), then reads it like any other;
-//   a.out: requests with one split are finished here (their normalised output
-//     is the result) and padded requests get zero rows; requests with more
-//     splits leave partials for the merge kernel.
+// The work of one (KV head kvh, split s, request b) workgroup of kWaves waves.
+// LDS comes from the caller: slot ids slot_lds[kWaves][kSuper], wave w's
+// accumulator rows (G * D floats) at red_acc + w * wstride, and red_ml.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s, int b,
+                                             int (*slot_lds)[kSuper], float* red_acc,
+                                             int wstride, float (*red_ml)[G][2]) {
   constexpr int LPR = lanes_per_row<T, D, G>();
   using Gm = Geo<T, D, LPR>;
   constexpr int CH = Gm::CH;
   constexpr int E = Gm::E;
-  __shared__ int slot_lds[kWaves][kSuper];
-  __shared__ float red_acc[kWaves][G][D];
-  __shared__ float red_ml[kWaves][G][2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int grp = lane / LPR;  // token group
   const int c = lane % LPR;    // this lane's first 16-byte chunk of a row
-  // KV head fastest: workgroups go to the XCDs round-robin by linear id, so
-  // each XCD gets the same KV head(s) of every split of every request, and
-  // requests with few splits do not pile their work onto a few XCDs.
-  const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
-
-  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
-    index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
 
   SplitCtx sc;
   if (!split_setup<T, D, G, 64 * kWaves>(a, b, kvh, s, sc)) return;
@@ -550,7 +568,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
       for (int k = 0; k < CH; ++k)
 #pragma unroll
         for (int e = 0; e < Gm::EPC; ++e)
-          red_acc[wave][h][(c + LPR * k) * Gm::EPC + e] = st.acc[h][k * Gm::EPC + e];
+          red_acc[wave * wstride + h * D + (c + LPR * k) * Gm::EPC + e] =
+              st.acc[h][k * Gm::EPC + e];
   }
   if (lane == 0) {
 #pragma unroll
@@ -561,7 +580,33 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   }
   __syncthreads();
 
-  finish_split<T, D, G, kWaves>(a, &red_acc[0][0][0], G * D, red_ml, b, kvh, s, sc.S);
+  finish_split<T, D, G, kWaves>(a, red_acc, wstride, red_ml, b, kvh, s, sc);
+}
+
+// One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B).
+// Optional fused steps:
+//   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
+//     index step for the whole batch;
+//   a.k_new / v_new: the wave whose share holds position L-1 first stores the
+//     new token's K/V row of this KV head at slot req_to_token[r_b, L-1]
+//     (skipped if that slot is out of range), then reads it like any other;
+//   a.out: requests with one split are finished here (their normalised output
+//     is the result) and padded requests get zero rows; requests with more
+//     splits leave partials for the merge kernel.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs a) {
+  __shared__ int slot_lds[kWaves][kSuper];
+  __shared__ float red_acc[kWaves][G][D];
+  __shared__ float red_ml[kWaves][G][2];
+  // KV head fastest: workgroups go to the XCDs round-robin by linear id, so
+  // each XCD gets the same KV head(s) of every split of every request, and
+  // requests with few splits do not pile their work onto a few XCDs.
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
+    index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
+  decode_split<T, D, G>(a, kvh, s, b, slot_lds, &red_acc[0][0][0], G * D, red_ml);
 }
 
 // One wave per (request, q head). Splits are taken 32 at a time: all 32
@@ -578,14 +623,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
-  int chunk;
-  const int S = split_count(L, a.split.max_splits, a.split.fixed_splits, a.split.split_tokens,
-                            &chunk);
-  // After the partial kernel ran with an output, requests with 0 or 1 split are
-  // already written.
-  if (a.merge_multi_only && S <= 1) return;
+  const Plan pl = plan_for(a, b);
+  const int S = pl.Sp + pl.S;  // prefix splits first, then the suffix splits
+  // After the partial kernel ran with an output, requests without prefix
+  // splits and with 0 or 1 suffix split are already written.
+  if (a.merge_multi_only && pl.Sp == 0 && pl.S <= 1) return;
   const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
   const float2* ml = (const float2*)(a.ml_part + 2 * part);
   const float* o = a.o_part + part * D + lane * PER;

@@ -87,12 +87,24 @@ struct KBlock {
   u32x4 v[MGeo<D>::NI];     // V: this lane's 16 bytes of each 1 KiB row group
 };
 
-template <int D>
+// Per-wave state for NTC column tiles of 16 query rows each.
+template <int D, int NTC>
 struct WaveState {
-  f32x4 o[MGeo<D>::DT];  // O^T: lane l holds d = 16 dt + 4 (l/16) + r of head l%16
-  f32x4 lsum;            // row sums (every element of the lane's column)
-  float m;               // stabiliser of head l%16, log2 units
+  f32x4 o[NTC][MGeo<D>::DT];  // O^T: lane l holds d = 16 dt + 4 (l/16) + r of column l%16
+  f32x4 lsum[NTC];            // row sums (every element of the lane's column)
+  float m[NTC];               // stabiliser of column l%16, log2 units
 };
+
+template <int D, int NTC>
+__device__ __forceinline__ void init_state(WaveState<D, NTC>& st) {
+#pragma unroll
+  for (int t = 0; t < NTC; ++t) {
+#pragma unroll
+    for (int dt = 0; dt < MGeo<D>::DT; ++dt) st.o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.lsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m[t] = -INFINITY;
+  }
+}
 
 // Loads of block i of a super-block into registers: K fragments, and V in
 // the layout its LDS tile is written in (lane l of row group t holds row
@@ -124,9 +136,10 @@ __device__ __forceinline__ void issue_block(KBlock<D>& kb, const int* slots, int
   }
 }
 
-template <int D>
-__device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>& kb,
-                                              char* vstage, const u32x4 (&qf)[MGeo<D>::KS],
+template <int D, int NTC>
+__device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBlock<D>& kb,
+                                              char* vstage,
+                                              const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                               float scale2, int key0, int whi, int lane) {
   using Gm = MGeo<D>;
   const int col = lane & 15;
@@ -136,50 +149,55 @@ __device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>&
 #pragma unroll
   for (int t = 0; t < Gm::NI; ++t)
     *(u32x4*)(vstage + Gm::RPI * t * Gm::ROW + 16 * lane) = kb.v[t];
-  // S^T: keys 16 kt + 4 quad + r, head col
-  f32x4 s[2];
+  u32x4 pf[NTC];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tc = 0; tc < NTC; ++tc) {
+    // S^T: keys 16 kt + 4 quad + r, column col of tile tc
+    f32x4 s[2];
 #pragma unroll
-    for (int ks = 0; ks < Gm::KS; ++ks) s[kt] = mfma16(kb.f[kt][ks], qf[ks], s[kt]);
-  }
-  float mx = -INFINITY;
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = key0 + 16 * kt + 4 * quad + r < whi ? s[kt][r] * scale2 : -INFINITY;
-      s[kt][r] = x;
-      mx = fmaxf(mx, x);
+      for (int ks = 0; ks < Gm::KS; ++ks) s[kt] = mfma16(kb.f[kt][ks], qf[tc][ks], s[kt]);
     }
-  if (__builtin_amdgcn_ballot_w64(mx > st.m + kTau) != 0) {
-    float x = fmaxf(mx, __shfl_xor(mx, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    const float mnew = fmaxf(st.m, x);
-    const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m - mnew);
-    st.lsum *= corr;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt) st.o[dt] *= corr;
-    st.m = mnew;
-  }
-  // P^T in the B-operand layout: slots 0..3 = key tile 0, 4..7 = key tile 1
-  const float mm = st.m == -INFINITY ? 0.f : st.m;
-  uint32_t w[4];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+      for (int r = 0; r < 4; ++r) {
+        const float x = key0 + 16 * kt + 4 * quad + r < whi ? s[kt][r] * scale2 : -INFINITY;
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    if (__builtin_amdgcn_ballot_w64(mx > st.m[tc] + kTau) != 0) {
+      float x = fmaxf(mx, __shfl_xor(mx, 16));
+      x = fmaxf(x, __shfl_xor(x, 32));
+      const float mnew = fmaxf(st.m[tc], x);
+      const float corr = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m[tc] - mnew);
+      st.lsum[tc] *= corr;
 #pragma unroll
-    for (int r = 0; r < 4; r += 2) {
-      const bf16x2_t pb = {(__bf16)__builtin_amdgcn_exp2f(s[kt][r] - mm),
-                           (__bf16)__builtin_amdgcn_exp2f(s[kt][r + 1] - mm)};
-      w[2 * kt + r / 2] = __builtin_bit_cast(uint32_t, pb);
+      for (int dt = 0; dt < Gm::DT; ++dt) st.o[tc][dt] *= corr;
+      st.m[tc] = mnew;
     }
-  const u32x4 pf = u32x4{w[0], w[1], w[2], w[3]};
-  st.lsum = mfma16(u32x4{kOnes, kOnes, kOnes, kOnes}, pf, st.lsum);
+    // P^T in the B-operand layout: slots 0..3 = key tile 0, 4..7 = key tile 1
+    const float mm = st.m[tc] == -INFINITY ? 0.f : st.m[tc];
+    uint32_t w[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const bf16x2_t pb = {(__bf16)__builtin_amdgcn_exp2f(s[kt][r] - mm),
+                             (__bf16)__builtin_amdgcn_exp2f(s[kt][r + 1] - mm)};
+        w[2 * kt + r / 2] = __builtin_bit_cast(uint32_t, pb);
+      }
+    pf[tc] = u32x4{w[0], w[1], w[2], w[3]};
+    st.lsum[tc] = mfma16(u32x4{kOnes, kOnes, kOnes, kOnes}, pf[tc], st.lsum[tc]);
+  }
   // O^T += V^T P^T. ds_read_b64_tr_b16 hands lane i of each 16-lane group
   // element i%4 of the 8-byte segments of lanes i/4, i/4+4, i/4+8, i/4+12;
   // pointing those at keys 4 quad + (0..3) (+16) and columns 16 dt + 4 (col%4)
-  // gives every lane its column's values in the key order of P^T.
+  // gives every lane its column's values in the key order of P^T. One V^T
+  // fragment serves every column tile.
   const int s4 = col & 3;
   const int r0 = 4 * quad + (col >> 2);
 #pragma unroll
@@ -188,15 +206,17 @@ __device__ __forceinline__ void compute_block(WaveState<D>& st, const KBlock<D>&
     const int half = 8 * (s4 & 1);
     const u32x2 lo = tr_read(vstage + swz<D>(r0, chunk) + half);
     const u32x2 hi = tr_read(vstage + swz<D>(r0 + 16, chunk) + half);
-    st.o[dt] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, st.o[dt]);
+    const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+    for (int tc = 0; tc < NTC; ++tc) st.o[tc][dt] = mfma16(va, pf[tc], st.o[tc][dt]);
   }
 }
 
 // NB consecutive 32-key blocks of one super-block, straight-line: block i's
 // loads are issued one block before its compute, into ring entry i % 2.
-template <int D, int NB>
-__device__ __forceinline__ void block_run(WaveState<D>& st, char* vstage, const int* slots,
-                                          int cb, int ce, const u32x4 (&qf)[MGeo<D>::KS],
+template <int D, int NTC, int NB>
+__device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, const int* slots,
+                                          int cb, int ce, const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                           const char* kbase, const char* vbase,
                                           int64_t row_stride, float scale2, int whi, int lane) {
   KBlock<D> kb[kRing];
@@ -207,29 +227,64 @@ __device__ __forceinline__ void block_run(WaveState<D>& st, char* vstage, const 
       issue_block<D>(kb[(i + 1) % 2], slots, i + 1, cb, ce, kbase, vbase, row_stride, lane);
     // keep the next block's loads ahead of this block's MFMAs
     __builtin_amdgcn_sched_barrier(0);
-    compute_block<D>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
+    compute_block<D, NTC>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
   }
 }
 
+// A wave's contiguous key range [wlo, whi) of one request row, in 128-key
+// super-blocks: the slot ids of each are staged in this wave's LDS row (the
+// next super-block's prefetched into registers meanwhile).
+template <int D, int NTC>
+__device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, char* vtile,
+                                          const int32_t* row, int n_slots, int wlo, int whi,
+                                          const u32x4 (&qf)[NTC][MGeo<D>::KS], const char* kbase,
+                                          const char* vbase, int64_t row_stride, float scale2,
+                                          int lane) {
+  constexpr int SBK = kSB * kBlk;  // keys per super-block
+  int ids[SBK / 64];
+  if (wlo < whi) {
+#pragma unroll
+    for (int j = 0; j < SBK / 64; ++j) ids[j] = row[min(wlo + lane + 64 * j, whi - 1)];
+  }
+  for (int cb = wlo; cb < whi; cb += SBK) {
+    const int ce = min(whi, cb + SBK);
+#pragma unroll
+    for (int j = 0; j < SBK / 64; ++j) slots[lane + 64 * j] = clamp_index(ids[j], n_slots);
+    // other lanes of this wave read these ids: order the LDS writes first
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int nb = cb + SBK;
+    if (nb < whi) {
+#pragma unroll
+      for (int j = 0; j < SBK / 64; ++j) ids[j] = row[min(nb + lane + 64 * j, whi - 1)];
+    }
+    switch (ceil_div(ce - cb, kBlk)) {
+#define PKV_DM_RUN(n)                                                                         \
+  case n:                                                                                     \
+    block_run<D, NTC, n>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, whi, \
+                         lane);                                                               \
+    break;
+      PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
+#undef PKV_DM_RUN
+      default: break;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
+  }
+}
+
+// The work of one (KV head kvh, split s, request b) workgroup of kW waves.
+// LDS comes from the caller: the per-wave V tiles vs0 (which also take the
+// waves' merge rows), slot ids slot_lds[kW][kSB * kBlk] and red_ml.
 template <int D, int G>
-__global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void mfma_split(const DecodeArgs& a, int kvh, int s, int b,
+                                           char (*vs0)[MGeo<D>::VST], int (*slot_lds)[kSB * kBlk],
+                                           float (*red_ml)[G][2]) {
   using Gm = MGeo<D>;
   static_assert(G <= 16, "one MFMA column per query head");
   static_assert(G * D * 4 <= Gm::VST, "a wave's merge rows fit in its V tile");
-  __shared__ __attribute__((aligned(1024))) char vs0[kW][Gm::VST];
-  __shared__ int slot_lds[kW][kSB * kBlk];
-  __shared__ float red_ml[kW][G][2];
-
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const int kvh = blockIdx.x;  // KV head fastest: XCD-balanced (see decode_impl.hpp)
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
-
-  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
-    index_step_block<64 * kW>(a, &slot_lds[0][0]);
 
   SplitCtx sc;
   if (!split_setup<bf16_t, D, G, 64 * kW>(a, b, kvh, s, sc)) return;
@@ -241,55 +296,21 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
 
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
-  constexpr int SBK = kSB * kBlk;  // keys per super-block
-  int ids[SBK / 64];
-  if (wlo < whi) {
-#pragma unroll
-    for (int j = 0; j < SBK / 64; ++j) ids[j] = sc.row[min(wlo + lane + 64 * j, whi - 1)];
-  }
   // Q^T fragments (B operand): head col, head_dim 8 quad + 32 ks .. +7; zero
   // for the columns past the group
   const int qh0 = kvh * G;
-  u32x4 qf[Gm::KS];
+  u32x4 qf[1][Gm::KS];
   const char* qp = (const char*)a.q + ((int64_t)b * a.n_q_heads + qh0 + min(col, G - 1)) * Gm::ROW +
                    16 * quad;
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
     const u32x4 v = *(const u32x4*)(qp + 64 * ks);
-    qf[ks] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
+    qf[0][ks] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
   }
-  const float scale2 = a.scale * kLog2e;
-  WaveState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.lsum = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-
-  int* slots = slot_lds[wave];
-  char* v0 = vs0[wave];
-  for (int cb = wlo; cb < whi; cb += SBK) {
-    const int ce = min(whi, cb + SBK);
-#pragma unroll
-    for (int j = 0; j < SBK / 64; ++j) slots[lane + 64 * j] = clamp_index(ids[j], sc.n_slots);
-    // other lanes of this wave read these ids: order the LDS writes first
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const int nb = cb + SBK;
-    if (nb < whi) {
-#pragma unroll
-      for (int j = 0; j < SBK / 64; ++j) ids[j] = sc.row[min(nb + lane + 64 * j, whi - 1)];
-    }
-    switch (ceil_div(ce - cb, kBlk)) {
-#define PKV_DM_RUN(n)                                                                         \
-  case n:                                                                                     \
-    block_run<D, n>(st, v0, slots, cb, ce, qf, kbase, vbase, sc.row_stride, scale2, whi,      \
-                    lane);                                                                    \
-    break;
-      PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
-#undef PKV_DM_RUN
-      default: break;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
-  }
+  WaveState<D, 1> st;
+  init_state(st);
+  wave_loop<D, 1>(st, slot_lds[wave], vs0[wave], sc.row, sc.n_slots, wlo, whi, qf, kbase, vbase,
+                  sc.row_stride, a.scale * kLog2e, lane);
 
   // Hand the wave's (m, l, O) to LDS; an empty wave leaves m = -inf, l = 0, O = 0.
   // The O rows go into this wave's V tile (its transpose reads have returned:
@@ -299,15 +320,28 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[dt][r];
+      for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[0][dt][r];
     if (quad == 0) {
-      red_ml[wave][col][0] = st.m;
-      red_ml[wave][col][1] = st.lsum[0];
+      red_ml[wave][col][0] = st.m[0];
+      red_ml[wave][col][1] = st.lsum[0][0];
     }
   }
   __syncthreads();
   finish_split<bf16_t, D, G, kW>(a, (const float*)&vs0[0][0], Gm::VST / 4, red_ml, b, kvh, s,
-                                 sc.S);
+                                 sc);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char vs0[kW][MGeo<D>::VST];
+  __shared__ int slot_lds[kW][kSB * kBlk];
+  __shared__ float red_ml[kW][G][2];
+  const int kvh = blockIdx.x;  // KV head fastest: XCD-balanced (see decode_impl.hpp)
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
+    index_step_block<64 * kW>(a, &slot_lds[0][0]);
+  mfma_split<D, G>(a, kvh, s, b, vs0, slot_lds, red_ml);
 }
 
 template <int D>

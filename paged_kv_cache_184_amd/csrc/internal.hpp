@@ -36,7 +36,20 @@ struct DecodeArgs {
   int32_t* kv_indptr_out;
   int32_t* loc_out;
   int32_t* splits_out;
+  // cascade (shared-prefix) decode; prefix_len null: no shared prefixes
+  const int32_t* prefix_len;     // [batch] shared-prefix length of each request (0: none)
+  const int32_t* group_indptr;   // [n_groups + 1] into group_members
+  const int32_t* group_members;  // request indices of each prefix group
+  int32_t n_groups;
+  int32_t max_members;           // bound on the members of one group
+  int32_t n_members;             // length of group_members
 };
+
+// Cascade decode partials: the groups' prefix splits and every request's own
+// (suffix) splits in one launch; the merge kernel follows.
+hipError_t launch_cascade_partials(const DecodeArgs& a, hipStream_t stream);
+// Prefix workgroups per group along the grid's z axis (16 / g members each).
+int cascade_tiles(int n_q_heads, int n_kv_heads, int max_members);
 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);

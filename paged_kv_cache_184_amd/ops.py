@@ -211,6 +211,35 @@ def paged_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: flo
     return out
 
 
+def make_prefix_groups(prefix_len: torch.Tensor, group_indptr: torch.Tensor,
+                       members: torch.Tensor, max_members: int) -> _lib.PrefixGroups:
+    """Descriptor of the shared-prefix groups of a batch (device int32 tensors)."""
+    for t, name in ((prefix_len, "prefix_len"), (group_indptr, "group_indptr"),
+                    (members, "members")):
+        _need(t.dtype == torch.int32 and t.is_contiguous() and t.is_cuda,
+              f"{name} must be a contiguous int32 device tensor")
+    g = _lib.PrefixGroups(prefix_len.data_ptr(), group_indptr.data_ptr(), members.data_ptr(),
+                          group_indptr.numel() - 1, max_members, members.numel(), 0)
+    g._tensors = (prefix_len, group_indptr, members)  # keep the buffers alive
+    return g
+
+
+def cascade_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta,
+                        groups: _lib.PrefixGroups, scale: float, split: SplitCfg,
+                        workspace: torch.Tensor, out=None, stream=None):
+    """Decode with each group's shared prefix read once (pkv_cascade_decode_attn)."""
+    pool = make_pool(k_pool, v_pool)
+    _q_check(q, pool, meta.batch)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype, "out")
+    _check(lib().pkv_cascade_decode_attn(C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                                         C.byref(meta), C.byref(groups), scale, split,
+                                         workspace.data_ptr(), workspace.numel(), out.data_ptr(),
+                                         _stream(stream)))
+    return out
+
+
 def decode_step(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float, split: SplitCfg,
                 workspace: torch.Tensor, k_new=None, v_new=None, kv_indptr_out=None, loc_out=None,
                 splits_out=None, out=None, stream=None):
@@ -323,6 +352,15 @@ def prepare_decode_step(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split,
                         _ptr(kv_indptr_out), _ptr(loc_out), _ptr(splits_out),
                         workspace.data_ptr(), workspace.numel(), out.data_ptr(), None,
                         keep=(pool, meta), stream=stream)
+
+
+def prepare_cascade_decode(q, k_pool, v_pool, layer, meta: BatchMeta, groups, scale, split,
+                           workspace, out, stream=None):
+    pool = make_pool(k_pool, v_pool)
+    return PreparedCall("pkv_cascade_decode_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                        C.byref(meta), C.byref(groups), scale, split, workspace.data_ptr(),
+                        workspace.numel(), out.data_ptr(), None, keep=(pool, meta, groups),
+                        stream=stream)
 
 
 def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None):

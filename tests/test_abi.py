@@ -103,6 +103,35 @@ def test_kv_store_other_rejects(lib):
     assert lib.pkv_last_error() == b""
 
 
+def test_cascade_rejects(lib):
+    def call(pool=None, groups=None, split=None, out=16, ws_bytes=1 << 20, hq=4):
+        pool = pool or _pool()
+        meta = _meta()
+        split = split or _split()
+        return lib.pkv_cascade_decode_attn(C.byref(pool), 0, 16, hq, C.byref(meta),
+                                           C.byref(groups) if groups is not None else None,
+                                           0.125, split, 256, ws_bytes, out, None)
+
+    def groups(**kw):
+        base = dict(prefix_len=16, group_indptr=32, members=48, n_groups=1, max_members=2,
+                    n_members=2, reserved=0)
+        base.update(kw)
+        return _lib.PrefixGroups(**base)
+
+    assert call(groups=None) == _lib.PKV_EINVAL
+    assert call(groups=groups(), pool=_pool(dtype=_lib.PKV_F32)) == _lib.PKV_EUNSUPPORTED
+    assert call(groups=groups(), split=_split(max_splits=1)) == _lib.PKV_EINVAL
+    assert call(groups=groups(max_members=0)) == _lib.PKV_EINVAL
+    assert call(groups=groups(max_members=65536)) == _lib.PKV_EINVAL
+    # g = 2: 8 members per prefix row; 9000 groups x 8 rows + batch > 65535
+    assert call(groups=groups(n_groups=9000, max_members=64)) == _lib.PKV_EINVAL
+    assert call(groups=groups(n_members=0)) == _lib.PKV_EINVAL
+    assert call(groups=groups(members=None)) == _lib.PKV_EINVAL
+    assert call(groups=groups(n_groups=-1)) == _lib.PKV_EINVAL
+    assert call(groups=groups(), out=None) == _lib.PKV_EINVAL
+    assert call(groups=groups(), ws_bytes=16) == _lib.PKV_EWORKSPACE
+
+
 def test_rope_kv_store_rejects(lib):
     p = _pool()
     f = lib.pkv_rope_kv_store
