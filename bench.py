@@ -164,7 +164,7 @@ class DecodeBench:
         self.cascade = None
         shared = getattr(b, "shared_rows", None)
         if shared is not None and len(shared) > 1:
-            P = 2048  # the ragged workload's shared prefix
+            P = int(b.shared_prefix)
             plen = np.zeros(B, np.int32)
             plen[shared] = P
             t = lambda x: torch.tensor(np.asarray(x, np.int32), device=dev)
@@ -502,14 +502,17 @@ def main():
             torch.cuda.empty_cache()
     if not args.no_batches:
         # batched decode workloads: ragged B=8 / B=32 with a shared 2048-token
-        # prefix, and B=64 lognormal lengths over a fragmented 2^21-slot pool
-        # (plus the same lengths in 16-token pages, to separate the cost of the
-        # token-granular scatter from the kernel's)
+        # prefix, B=64 lognormal lengths over a fragmented 2^21-slot pool (plus
+        # the same lengths in 16-token pages, to separate the cost of the
+        # token-granular scatter from the kernel's), and B=32 requests that all
+        # share a 4096-token prefix (plain vs cascade attention)
         for name, make in (("ragged_b8", lambda: W.ragged_decode(8, n_layers=8)),
                            ("ragged_b32", lambda: W.ragged_decode(32, n_layers=8)),
                            ("large_b64", lambda: W.large_batch_decode(n_layers=4)),
                            ("large_b64_pages16",
-                            lambda: W.large_batch_decode(n_layers=4, layout="pages16"))):
+                            lambda: W.large_batch_decode(n_layers=4, layout="pages16")),
+                           ("shared_prefix_b32",
+                            lambda: W.shared_prefix_decode(32, 4096, n_layers=8))):
             db = DecodeBench(make(), split_tokens=0, seed=184_010 + len(name))
             steps = max(10, args.steps // 4)
             db.mode = "fused"

@@ -223,6 +223,28 @@ def ragged_decode(batch: int, n_layers: int = 1) -> PagedBatch:
     out = _finish(f"ragged_decode_b{batch}", n_layers, n_slots, 32, 8, 128, "bf16",
                   1.0 / np.sqrt(128.0), lens, np.ones(batch, np.int32), lists, rng)
     out.shared_rows = shared  # type: ignore[attr-defined]
+    out.shared_prefix = prefix_len  # type: ignore[attr-defined]
+    return out
+
+
+def shared_prefix_decode(batch: int = 32, prefix_len: int = 4096,
+                         n_layers: int = 1) -> PagedBatch:
+    """Every request of the batch shares one prefix of prefix_len keys (the
+    same slots) and has a private tail of U{32..512} keys; shuffled 16-pages in
+    a 2^18-slot pool; 32 q / 8 KV heads, head_dim 128, bf16. A case where the
+    prefix dominates the logical K/V bytes."""
+    k = 6
+    rng = np.random.default_rng(SEED_BASE + k + 1 + batch)
+    n_slots = 1 << 18
+    tails = rng.integers(32, 512, size=batch, endpoint=True)
+    lists_all = _pages16_slots(rng, n_slots, [prefix_len] + [int(t) for t in tails],
+                               reserve=PAGE)
+    lists = [np.concatenate([lists_all[0], lists_all[1 + b]]) for b in range(batch)]
+    lens = tails + prefix_len
+    out = _finish(f"shared_prefix_decode_b{batch}", n_layers, n_slots, 32, 8, 128, "bf16",
+                  1.0 / np.sqrt(128.0), lens, np.ones(batch, np.int32), lists, rng)
+    out.shared_rows = np.arange(batch)  # type: ignore[attr-defined]
+    out.shared_prefix = prefix_len  # type: ignore[attr-defined]
     return out
 
 
