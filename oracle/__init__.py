@@ -34,3 +34,12 @@ from .paged_attention import (  # noqa: F401
     apply_rope,
     rope_kv_store,
 )
+from .fp8_kv import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_decode,
+    e4m3_encode,
+    quantize,
+    dequantize,
+    kv_store_fp8,
+    decode_attention_fp8,
+)

@@ -450,6 +450,152 @@ def pin_rope_kv_store(O, seed=23):
     assert np.array_equal(k2[1, keep], kp[1, keep]) and np.array_equal(v2[1, keep], vp[1, keep])
 
 
+# ------------------------------------------------------- FP8 (E4M3) KV pins
+
+GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "fp8_e4m3.json")
+
+
+def _torch_fp8_decode(codes):
+    """torch's float8_e4m3fn -> float64 (the library routine)."""
+    c = torch.from_numpy(np.ascontiguousarray(np.asarray(codes, np.uint8)))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_fp8_encode(x32):
+    """torch's float32 -> float8_e4m3fn code (round to nearest even; in range only)."""
+    return torch.from_numpy(np.asarray(x32, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def pin_e4m3_decode_library(O):
+    """Every one of the 256 codes decodes as torch's float8_e4m3fn does."""
+    codes = np.arange(256, dtype=np.uint8)
+    mine, ref = O.e4m3_decode(codes), _torch_fp8_decode(codes)
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def pin_e4m3_spec_values(O):
+    """Hand-derived values of the OFP8 E4M3 definition (tests/golden/fp8_e4m3.json)."""
+    with open(GOLDEN_FP8) as f:
+        g = json.load(f)
+    for code, val in g["decode"].items():
+        assert O.e4m3_decode([int(code, 16)])[0] == val, code
+    for code in g["decode_nan"]:
+        assert np.isnan(O.e4m3_decode([int(code, 16)])[0]), code
+    z = O.e4m3_decode([int(g["decode_negative_zero"], 16)])[0]
+    assert z == 0.0 and np.signbit(z)
+    for x, code in g["encode"].items():
+        if not x.startswith("_"):
+            assert O.e4m3_encode(np.float32([float(x)]))[0] == int(code, 16), x
+
+
+def pin_e4m3_encode_library(O, seed=30):
+    """In range, encoding equals torch's float32 -> float8_e4m3fn on random
+    values, on every midpoint between neighbouring codes and one fp32 ulp to
+    either side of each midpoint."""
+    rng = np.random.default_rng(seed)
+    pos = _torch_fp8_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    x = np.concatenate([
+        rng.uniform(-448, 448, 20000).astype(np.float32),
+        (rng.standard_normal(20000) * np.exp2(rng.integers(-12, 8, 20000))).astype(np.float32),
+        mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+        -mids, np.float32([0.0, -0.0, 448.0, -448.0])])
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(O.e4m3_encode(x), _torch_fp8_encode(x))
+
+
+def pin_e4m3_saturation_and_nan(O):
+    """Closed forms: magnitudes at or beyond 448, infinities included,
+    saturate to the largest finite code of their sign; NaN encodes to a NaN
+    code; every finite code survives a decode-encode round trip."""
+    big = np.float32([448.0, 449.0, 463.9, 464.0, 480.0, 1e6, np.inf])
+    assert (O.e4m3_encode(big) == 0x7E).all()
+    assert (O.e4m3_encode(-big) == 0xFE).all()
+    assert np.isnan(O.e4m3_decode(O.e4m3_encode(np.float32([np.nan])))).all()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes).astype(np.float32)), codes)
+
+
+def pin_quantize_fp32_quotient(O, seed=31):
+    """Quantisation decides on the fp32 quotient: it equals torch's fp32
+    division followed by torch's float8 conversion, also on constructed x whose
+    fp32 quotient lands exactly on a midpoint while the exact quotient does not;
+    power-of-two scales are exact and reduce to encoding x / 2^k."""
+    rng = np.random.default_rng(seed)
+    pos = _torch_fp8_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    xs, ss = [], []
+    for _ in range(400):
+        s = np.float32(rng.uniform(0.3, 3.0))
+        m = mids[rng.integers(8, len(mids) - 4)]
+        x0 = np.float32(m * float(s))
+        for k in range(-6, 7):
+            x = np.float32(x0 + k * np.spacing(x0))
+            q32 = np.float32(x) / s
+            if float(q32) == m and float(x) / float(s) != m:
+                xs.append(x)
+                ss.append(s)
+    assert len(xs) >= 20  # near-ties where the fp64 quotient would decide differently
+    for x, s in zip(xs, ss):
+        ref = _torch_fp8_encode((torch.tensor([x], dtype=torch.float32) /
+                                 torch.tensor(s, dtype=torch.float32)).numpy())
+        assert O.quantize(np.float32([x]), s)[0] == ref[0], (x, s)
+    x = rng.uniform(-400, 400, 5000).astype(np.float32)
+    for k in (-3, 0, 2):
+        assert np.array_equal(O.quantize(x * np.float32(2.0 ** k), 2.0 ** k), O.e4m3_encode(x))
+    s = np.float32(0.37)
+    ref = _torch_fp8_encode(torch.from_numpy(x / 200).div(torch.tensor(s)).numpy())
+    assert np.array_equal(O.quantize(x / 200, s), ref)
+
+
+def pin_kv_store_fp8(O, seed=32):
+    """Quantised store: the addressed rows of the addressed layer hold torch's
+    quantisation of the new rows (K and V each under their own scale); every
+    other byte is unchanged; negative locations are skipped."""
+    rng = np.random.default_rng(seed)
+    kp = rng.integers(0, 256, (3, 40, 2, 8)).astype(np.uint8)
+    vp = rng.integers(0, 256, (3, 40, 2, 8)).astype(np.uint8)
+    kn = (rng.standard_normal((5, 2, 8)) * 2).astype(np.float32)
+    vn = (rng.standard_normal((5, 2, 8)) * 2).astype(np.float32)
+    scales = np.float32([[1.0, 1.0], [0.05, 0.03], [2.0, 4.0]])  # |x| / scale stays < 448
+    loc = np.array([39, 4, -1, 0, 21], np.int32)
+    k2, v2 = O.kv_store_fp8(kp, vp, 1, kn, vn, loc, scales)
+    touched = {39: 0, 4: 1, 0: 3, 21: 4}
+    for L in range(3):
+        for sl in range(40):
+            if L == 1 and sl in touched:
+                t = touched[sl]
+                assert np.array_equal(k2[L, sl], _torch_fp8_encode(kn[t] / scales[1, 0]))
+                assert np.array_equal(v2[L, sl], _torch_fp8_encode(vn[t] / scales[1, 1]))
+            else:
+                assert np.array_equal(k2[L, sl], kp[L, sl])
+                assert np.array_equal(v2[L, sl], vp[L, sl])
+
+
+def pin_decode_fp8_library(O, seed=33):
+    """Decode over code pools equals torch SDPA (fp64) over K/V dequantised
+    by torch (float8_e4m3fn -> float64, times the layer's scales)."""
+    b, v = small_batch(seed, B=3, hq=4, hkv=2, d=16)
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = rng.choice(finite, size=v.k_pool.shape).astype(np.uint8)
+    vc = rng.choice(finite, size=v.v_pool.shape).astype(np.uint8)
+    scales = np.float32([[0.01, 0.5], [0.02, 0.25]])
+    out = O.decode_attention_fp8(v.q, kc, vc, scales, 1, b.req_to_token, b.req_pool_indices,
+                                 b.seq_lens, b.scale)
+    for i in range(b.batch):
+        L = int(b.seq_lens[i])
+        slots = b.req_to_token[b.req_pool_indices[i], :L]
+        K = _torch_fp8_decode(kc[1, slots]) * float(scales[1, 0])
+        V = _torch_fp8_decode(vc[1, slots]) * float(scales[1, 1])
+        ref = sdpa_reference(v.q[i:i + 1], K, V, b.scale, b.group)[0]
+        np.testing.assert_allclose(out[i], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_decode_vs_sdpa, pin_prefill_vs_sdpa, pin_golden_two_keys, pin_golden_prefill,
     pin_closed_forms, pin_gqa_mapping, pin_slot_permutation, pin_split_merge,
@@ -457,5 +603,7 @@ ALL_PINS = [
     pin_scale, pin_padded_rows, pin_index_golden, pin_kv_indptr_properties, pin_split_golden,
     pin_split_properties, pin_kv_store_golden, pin_kv_store_bytes, pin_rope_golden,
     pin_rope_complex, pin_rope_half_split_is_permuted_interleaved, pin_rope_standard_table,
-    pin_rope_kv_store,
+    pin_rope_kv_store, pin_e4m3_decode_library, pin_e4m3_spec_values, pin_e4m3_encode_library,
+    pin_e4m3_saturation_and_nan, pin_quantize_fp32_quotient, pin_kv_store_fp8,
+    pin_decode_fp8_library,
 ]

@@ -13,7 +13,9 @@ import pytest
 
 from tests import oracle_pins as P
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "paged_attention.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle")
+SRC = os.path.join(ORACLE_DIR, "paged_attention.py")
+SRC_FP8 = os.path.join(ORACLE_DIR, "fp8_kv.py")
 
 MUTATIONS = {
     "gqa_modulo": ("K[:, h // g]", "K[:, h % Hkv]"),
@@ -55,19 +57,64 @@ MUTATIONS = {
 }
 
 
-def mutated_oracle(old, new):
-    with open(SRC) as f:
-        text = f.read()
-    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
+# planted mistakes in the FP8 module (oracle/fp8_kv.py)
+FP8_MUTATIONS = {
+    "e4m3_bias_8": ("np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    "e4m3_subnormal_scale": ("(m / 8.0) * 2.0 ** -6", "(m / 8.0) * 2.0 ** -7"),
+    "e4m3_no_nan_code": ("mag = np.where((e == 15) & (m == 7), np.nan, mag)", "pass"),
+    "e4m3_ties_up": ("np.where(lo % 2 == 0, lo, hi)", "hi"),
+    "e4m3_ties_down": ("np.where(lo % 2 == 0, lo, hi)", "lo"),
+    "e4m3_sign_dropped": ("code = code | np.where(np.signbit(x), 0x80, 0)", "code = code"),
+    "e4m3_nan_to_zero": ("code = np.where(np.isnan(x), 0x7F, code)", "code = code"),
+    "quantize_multiplies": ("x32 / np.float32(scale)", "x32 * np.float32(scale)"),
+    "quantize_fp64_quotient": ("x32 / np.float32(scale)",
+                               "np.asarray(x, np.float64) / float(scale)"),
+    "store_scales_swapped": ("ks, vs = (np.float32(s) for s in", "vs, ks = (np.float32(s) for s in"),
+    "store_layer0_scales": ("np.asarray(kv_scales, np.float32)[layer])",
+                            "np.asarray(kv_scales, np.float32)[0])"),
+    "store_negative_loc_fp8": ("        if loc[t] >= 0:\n            k_out[layer, loc[t]] = quantize",
+                               "        if True:\n            k_out[layer, loc[t]] = quantize"),
+    "decode_fp8_ignores_v_scale": ("vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)",
+                                   "vp = dequantize(np.asarray(v_codes)[layer:layer + 1], 1.0)"),
+    "decode_fp8_k_scale_for_v": ("kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)",
+                                 "kp = dequantize(np.asarray(k_codes)[layer:layer + 1], vs)"),
+    "decode_fp8_layer0": ("kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)",
+                          "kp = dequantize(np.asarray(k_codes)[0:1], ks)"),
+}
+
+
+def mutated_oracle(old, new, target=None):
+    """The oracle's two modules executed into one namespace, with `old`
+    replaced by `new` in the target module's source."""
+    target = target or SRC
+    texts = {}
+    for path in (SRC, SRC_FP8):
+        with open(path) as f:
+            texts[path] = f.read()
+    assert texts[target].count(old) >= 1, f"mutation anchor not found: {old!r}"
+    texts[target] = texts[target].replace(old, new)
+    # the FP8 module's relative import resolves to the (possibly mutated) namespace
+    texts[SRC_FP8] = texts[SRC_FP8].replace("from .paged_attention import decode_attention\n", "")
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(text.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    exec(compile(texts[SRC], "oracle_mutant", "exec"), mod.__dict__)
+    exec(compile(texts[SRC_FP8], "oracle_mutant_fp8", "exec"), mod.__dict__)
     return mod
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
+CASES = {**{k: (o, n, SRC) for k, (o, n) in MUTATIONS.items()},
+         **{k: (o, n, SRC_FP8) for k, (o, n) in FP8_MUTATIONS.items()}}
+
+
+def test_unmutated_namespace_passes_every_pin():
+    mod = mutated_oracle("", "")
+    for pin in P.ALL_PINS:
+        pin(mod)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
 def test_mutation_is_caught(name):
-    old, new = MUTATIONS[name]
-    mutant = mutated_oracle(old, new)
+    old, new, target = CASES[name]
+    mutant = mutated_oracle(old, new, target)
     caught = []
     for pin in P.ALL_PINS:
         try:
