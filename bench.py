@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-batches", action="store_true", help="skip the batched decode workloads")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) KV decode line")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--graph", action="store_true", help="also time HIP-graph replay")
     p.add_argument("--profile", action="store_true",
@@ -100,29 +101,39 @@ def spin_cycles_per_s() -> float:
 class DecodeBench:
     """Device state of one B=1 decode workload and its prepared library calls."""
 
-    def __init__(self, b, split_tokens: int, seed: int):
+    def __init__(self, b, split_tokens: int, seed: int, kv: str = "bf16"):
         """b: a decode workload (one new token per request) with n_layers
-        identical layers to rotate over."""
+        identical layers to rotate over. kv: "bf16" pools, or "fp8" pools of
+        E4M3 codes (N(0,1) values under a scale of 1/64 per layer, saturated)."""
         import torch
 
         from paged_kv_cache_184_amd import ops
 
         self.torch, self.ops = torch, ops
         self.b = b
+        self.kv = kv
+        self.kv_es = 1 if kv == "fp8" else 2  # bytes per stored K/V element
         ctx = int(b.seq_lens.max())
         dev = "cuda"
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
         shape = (b.n_layers, b.n_slots, b.n_kv_heads, b.head_dim)
-        self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
-        self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
         live = torch.from_numpy(b.live_slots).to(dev).long()
-        kv = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
-        kv = kv.to(torch.bfloat16)
+        vals = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
+        if kv == "fp8":
+            self.kv_scales = torch.full((b.n_layers, 2), 1.0 / 64, dtype=torch.float32, device=dev)
+            self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)  # NaN codes
+            self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+            vals = (vals * 64).clamp_(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            self.kv_scales = None
+            self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+            self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+            vals = vals.to(torch.bfloat16)
         for layer in range(b.n_layers):  # identical layers
-            self.k_pool[layer, live] = kv[0]
-            self.v_pool[layer, live] = kv[1]
-        del kv
+            self.k_pool[layer, live] = vals[0]
+            self.v_pool[layer, live] = vals[1]
+        del vals
         B = b.batch
         self.q = torch.randn((B, b.n_q_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
         self.k_new = torch.randn((B, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
@@ -150,20 +161,21 @@ class DecodeBench:
                 ops.prepare_metadata(self.meta, ops.PKV_MODE_DECODE, self.split, self.kv_indptr,
                                      self.loc, self.splits),
                 ops.prepare_kv_store(self.k_pool, self.v_pool, layer, self.k_new, self.v_new,
-                                     self.loc),
+                                     self.loc, kv_scales=self.kv_scales),
                 ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale,
-                                   self.split, self.ws, self.out, stage="all"),
+                                   self.split, self.ws, self.out, stage="all",
+                                   kv_scales=self.kv_scales),
             ))
             self.fused.append(ops.prepare_decode_step(
                 self.q, self.k_pool, self.v_pool, layer, self.meta, b.scale, self.split, self.ws,
                 self.out, k_new=self.k_new, v_new=self.v_new, kv_indptr_out=self.kv_indptr,
-                loc_out=self.loc, splits_out=self.splits))
+                loc_out=self.loc, splits_out=self.splits, kv_scales=self.kv_scales))
         self.mode = "fused"
         # attention alone, plain or cascade (shared prefixes read once per group)
         self.attn_only = [c[2] for c in self.calls]
         self.cascade = None
         shared = getattr(b, "shared_rows", None)
-        if shared is not None and len(shared) > 1:
+        if shared is not None and len(shared) > 1 and kv == "bf16":
             P = int(b.shared_prefix)
             plen = np.zeros(B, np.int32)
             plen[shared] = P
@@ -175,12 +187,12 @@ class DecodeBench:
                                                        self.split, self.ws, self.out)
                             for layer in range(b.n_layers)]
 
-    # algorithmic bytes
+    # algorithmic bytes (K/V at kv_es bytes per element)
     def kv_bytes(self) -> int:
-        return self.b.kv_bytes_logical()
+        return self.b.kv_bytes_logical() * self.kv_es // 2
 
     def kv_bytes_unique(self) -> int:
-        return self.b.kv_bytes_unique()
+        return self.b.kv_bytes_unique() * self.kv_es // 2
 
     def partial_kernel_bytes(self) -> int:
         b = self.b
@@ -192,7 +204,7 @@ class DecodeBench:
         the new token's K/V read and stored."""
         b = self.b
         return (self.partial_kernel_bytes() + b.batch * b.n_q_heads * b.head_dim * 2 +
-                2 * 2 * b.batch * b.n_kv_heads * b.head_dim * 2)
+                2 * b.batch * b.n_kv_heads * b.head_dim * (2 + self.kv_es))
 
     def step(self, i: int):
         """One decode step for layer i mod n_layers."""
@@ -242,7 +254,7 @@ class DecodeBench:
         torch = self.torch
         parts = [self.ops.prepare_decode(self.q, self.k_pool, self.v_pool, layer, self.meta,
                                          self.b.scale, self.split, self.ws, self.out,
-                                         stage="partials")
+                                         stage="partials", kv_scales=self.kv_scales)
                  for layer in range(self.b.n_layers)]
         for i in range(warmup):
             parts[i % len(parts)]()
@@ -301,11 +313,19 @@ class DecodeBench:
         L = int(b.seq_lens[0])
         slots = b.req_to_token[b.req_pool_indices[0], :L]
         idx = self.torch.from_numpy(slots.astype(np.int64)).to("cuda")
-        k = self.k_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
-        v = self.v_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
         r2t = np.arange(L, dtype=np.int32)[None]
-        ref = O.decode_attention(self.q[:1].float().cpu().numpy(), k, v, 0, r2t,
-                                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
+        q = self.q[:1].float().cpu().numpy()
+        if self.kv == "fp8":
+            k = self.k_pool[layer].index_select(0, idx).cpu().numpy()[None]
+            v = self.v_pool[layer].index_select(0, idx).cpu().numpy()[None]
+            ref = O.decode_attention_fp8(q, k, v, self.kv_scales.cpu().numpy(), 0, r2t,
+                                         np.array([0], np.int32), np.array([L], np.int32),
+                                         b.scale)
+        else:
+            k = self.k_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
+            v = self.v_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
+            ref = O.decode_attention(q, k, v, 0, r2t, np.array([0], np.int32),
+                                     np.array([L], np.int32), b.scale)
         return float(np.abs(self.out[:1].float().cpu().numpy() - ref).max())
 
     def oracle_inputs(self):
@@ -500,6 +520,28 @@ def main():
         else:
             del db
             torch.cuda.empty_cache()
+    if not args.no_fp8 and head is not None:
+        # the headline context on an FP8 (E4M3) pool: half the K/V bytes
+        ctx = args.headline
+        db8 = DecodeBench(W.b1_decode(ctx, n_layers=8), split_tokens=args.split_tokens,
+                          seed=184_020 + ctx, kv="fp8")
+        db8.mode = "fused"
+        step8, _ = db8.run(args.steps, args.warmup)
+        part8 = db8.run_partials(args.steps, args.warmup)
+        entry = {
+            "us_per_step": round(step8 * 1e3, 2),
+            "kv_gbs": round(db8.kv_bytes() / (step8 * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * db8.step_bytes() / (step8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "partial_kernel_us": round(part8 * 1e3, 2),
+            "partial_kernel_gbs": round(db8.partial_kernel_bytes() / (part8 * 1e-3) / 1e9, 1),
+            "step_speedup_vs_bf16": round(head[1] / step8, 3),
+            "splits": int(db8.split.max_splits), "split_tokens": int(db8.split.split_tokens),
+            "max_abs_err": db8.check(),
+        }
+        detail[f"{ctx // 1024}k_fp8"] = entry
+        print(f"# ctx {ctx} fp8: {entry}", file=sys.stderr, flush=True)
+        del db8
+        torch.cuda.empty_cache()
     if not args.no_batches:
         # batched decode workloads: ragged B=8 / B=32 with a shared 2048-token
         # prefix, B=64 lognormal lengths over a fragmented 2^21-slot pool (plus

@@ -29,7 +29,11 @@
  *
  * Supported: dtype F32 or BF16 (Q, K, V and output share it; accumulation is
  * always fp32; prefill is BF16 only), head_dim 64 or 128, group size
- * n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}.
+ * n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}. FP8_E4M3 pools (one-byte codes
+ * with per-layer K and V scales, see pkv_kv_pool) hold K/V for the decode
+ * entry points and pkv_kv_store; there q, the new K/V rows and the output are
+ * BF16 (P4, bullet on the fp8 MMA test kernel of the attention kernels; the
+ * code format is the OCP 8-bit floating point E4M3 encoding).
  *
  * Memory safety: kernels clamp every device-supplied index to the buffer it
  * addresses (slots to [0, n_slots), request rows to [0, n_req_rows), positions
@@ -49,13 +53,13 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* ---- status codes ---------------------------------------------------- */
 typedef int32_t pkv_status;
 #define PKV_OK 0
 #define PKV_EINVAL 1       /* null pointer, negative size, index out of range, bad mode */
-#define PKV_EDTYPE 2       /* dtype code not F32 / BF16 */
+#define PKV_EDTYPE 2       /* dtype code not F32 / BF16 / FP8_E4M3 */
 #define PKV_ESHAPE 3       /* inconsistent shapes, e.g. n_q_heads % n_kv_heads != 0 */
 #define PKV_EALIGN 4       /* tensor pointer not 16-byte aligned, workspace not 256-byte aligned */
 #define PKV_EWORKSPACE 5   /* workspace smaller than pkv_decode_workspace_bytes() */
@@ -65,6 +69,7 @@ typedef int32_t pkv_status;
 /* ---- dtypes and modes -------------------------------------------------- */
 #define PKV_F32 0
 #define PKV_BF16 1
+#define PKV_FP8_E4M3 2 /* pools only: OCP E4M3 codes (bias 7, subnormals, NaN = S.1111.111, max 448) */
 
 #define PKV_MODE_DECODE 0
 #define PKV_MODE_PREFILL 1
@@ -77,7 +82,12 @@ typedef int32_t pkv_status;
 /* ---- descriptors ------------------------------------------------------- */
 
 /* The KV pools. k and v are device pointers, 16-byte aligned, to contiguous
- * [n_layers, n_slots, n_kv_heads, head_dim] tensors of `dtype`. Owned by the caller. */
+ * [n_layers, n_slots, n_kv_heads, head_dim] tensors of `dtype`. Owned by the caller.
+ * kv_scales: FP8_E4M3 pools only (required there, 8-byte aligned, ignored
+ * otherwise): device fp32 [n_layers, 2] = (k_scale, v_scale) of each layer,
+ * read by the kernels at run time. A code c of layer l's K pool stands for
+ * e4m3(c) * k_scale[l] (V likewise); stores write the code nearest to the fp32
+ * quotient x / scale (ties to even, magnitudes beyond 448 saturated). */
 typedef struct pkv_kv_pool {
   void* k;
   void* v;
@@ -87,6 +97,7 @@ typedef struct pkv_kv_pool {
   int32_t head_dim;
   int32_t dtype;
   int32_t reserved;
+  const float* kv_scales;
 } pkv_kv_pool;
 
 /* Per-batch metadata; all arrays are int32 device pointers owned by the caller.
@@ -140,8 +151,11 @@ const char* pkv_last_error(void);
  * (P1, bullet on single advanced indexing buffer[layer_id, loc]). Negative
  * locations (padded rows) and locations >= n_slots are skipped. The copy is
  * bit-exact; locations must be unique within one call (duplicates race).
- * k_new, v_new: device [n_tokens, n_kv_heads, head_dim] of the pool dtype,
- * 16-byte aligned. loc: device int32 [n_tokens]. n_tokens == 0 is a no-op. */
+ * k_new, v_new: device [n_tokens, n_kv_heads, head_dim] of the pool dtype
+ * (BF16 for an FP8_E4M3 pool, whose rows are quantised under the layer's
+ * scales, the code of fl32(x / scale) rounded to nearest even and saturated
+ * at +-448, NaN to a NaN code), 16-byte aligned. loc: device int32
+ * [n_tokens]. n_tokens == 0 is a no-op. */
 pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_new,
                         const void* v_new, const int32_t* loc, int64_t n_tokens,
                         hipStream_t stream);
@@ -161,7 +175,8 @@ pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_ne
  * aligned; q_out may equal q (in place); both NULL to rotate only k.
  * k_new, v_new: device [n_tokens, n_kv_heads, head_dim], 16-byte aligned, not
  * modified. positions, loc: device int32 [n_tokens]. freqs_cis: device float
- * [max_pos, head_dim/2, 2], 8-byte aligned. */
+ * [max_pos, head_dim/2, 2], 8-byte aligned. F32 and BF16 pools (FP8_E4M3:
+ * PKV_EUNSUPPORTED). */
 pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* q, void* q_out,
                              int32_t n_q_heads, const void* k_new, const void* v_new,
                              const int32_t* positions, const float* freqs_cis, int32_t max_pos,
@@ -210,9 +225,12 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head
  * split partials in the workspace (a3) followed by a log-sum-exp merge (a4);
  * a request with a single split is finished by the first kernel, the merge
  * launch combines the others. Rows with L_b = 0 produce zeros.
- * q, out: device [batch, n_q_heads, head_dim] of the pool dtype, 16-byte
- * aligned; out is rounded to nearest-even. For BF16 the P.V products use P
- * rounded to bf16 and the row sums use the same rounded values. The result is
+ * q, out: device [batch, n_q_heads, head_dim] of the pool dtype (BF16 for an
+ * FP8_E4M3 pool), 16-byte aligned; out is rounded to nearest-even. For BF16
+ * the P.V products use P rounded to bf16 and the row sums use the same
+ * rounded values. FP8_E4M3: K and V are the codes' values times the layer's
+ * scales (codes widened exactly to bf16; the K scale joins the softmax
+ * scale, the V scale multiplies the split outputs). The result is
  * bit-identical run to run and does not depend on where the slots sit in the
  * pool. Calls that share a workspace must not overlap in time. */
 pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
@@ -224,7 +242,7 @@ pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const v
  * pointer is non-NULL: kv_indptr_out [batch+1], loc_out [batch], splits_out
  * [batch], as pkv_build_metadata in DECODE mode), the store of each request's
  * new token (k_new, v_new: device [batch, n_kv_heads, head_dim] of the pool
- * dtype, 16-byte aligned, stored at slot req_to_token[r_b, L_b-1] as
+ * dtype, BF16 for FP8_E4M3 pools; 16-byte aligned, stored at slot req_to_token[r_b, L_b-1] as
  * pkv_kv_store would with those locations; both NULL to skip the store) and
  * the attention of pkv_paged_decode_attn, which reads the stored rows. The new
  * tokens' slots must not be read by another request of the same call. */
@@ -288,7 +306,8 @@ pkv_status pkv_decode_partials(const pkv_kv_pool* pool, int32_t layer, const voi
  * wrote there in the documented layout):
  *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s exp(m_s - max_s' m_s').
  * A request with one split gets that split's o unchanged (rounded to the output
- * dtype), as pkv_paged_decode_attn does. */
+ * dtype), as pkv_paged_decode_attn does. dtype is the output's: F32 or BF16
+ * (BF16 after an FP8_E4M3 pool). */
 pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32_t head_dim,
                             int32_t dtype, pkv_split_cfg split, const void* workspace,
                             size_t ws_bytes, void* out, hipStream_t stream);
@@ -302,7 +321,7 @@ pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32
  * K/V must already be stored (pkv_kv_store). q, out: device
  * [total_q, n_q_heads, head_dim], 16-byte aligned. max_q_len >= every n_b sizes
  * the grid (rows i >= max_q_len are not computed). BF16 pools only (any other
- * dtype returns PKV_EUNSUPPORTED): QK^T and PV run on bf16 MFMA with fp32
+ * dtype, FP8_E4M3 included, returns PKV_EUNSUPPORTED): QK^T and PV run on bf16 MFMA with fp32
  * accumulation, P is rounded to bf16 for PV and the row sums use those rounded
  * values; any finite scale, including 0 and negative values. Bit-identical run
  * to run and independent of where the slots sit in the pool. */

@@ -17,8 +17,10 @@ PKV_EWORKSPACE = 5
 PKV_EUNSUPPORTED = 6
 PKV_EHIP = 7
 
+PKV_ABI_VERSION = 2
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 PKV_MODE_DECODE = 0
 PKV_MODE_PREFILL = 1
 PKV_SPLIT_ALIGN = 16
@@ -37,7 +39,7 @@ EXPORTS = (
 class KVPool(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_layers", C.c_int64),
                 ("n_slots", C.c_int64), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("dtype", C.c_int32), ("reserved", C.c_int32)]
+                ("dtype", C.c_int32), ("reserved", C.c_int32), ("kv_scales", C.c_void_p)]
 
 
 class BatchMeta(C.Structure):

@@ -40,14 +40,18 @@ pkv_status hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+int elem_bytes(int32_t dtype) { return dtype == PKV_FP8_E4M3 ? 1 : dtype == PKV_BF16 ? 2 : 4; }
 
 constexpr int32_t kMaxBatch = 65535;  // grid y/z limit of the decode and prefill launches
 
 pkv_status check_pool(const pkv_kv_pool* pool, int32_t layer) {
   if (!pool) return fail(PKV_EINVAL, "pool is NULL");
-  if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16)
-    return fail(PKV_EDTYPE, "pool dtype %d is not PKV_F32 or PKV_BF16", pool->dtype);
+  if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16 && pool->dtype != PKV_FP8_E4M3)
+    return fail(PKV_EDTYPE, "pool dtype %d is not PKV_F32, PKV_BF16 or PKV_FP8_E4M3",
+                pool->dtype);
+  if (pool->dtype == PKV_FP8_E4M3 &&
+      (!pool->kv_scales || ((uintptr_t)pool->kv_scales & 7u) != 0))
+    return fail(PKV_EINVAL, "an FP8_E4M3 pool needs kv_scales (8-byte aligned device fp32)");
   if (!pool->k || !pool->v) return fail(PKV_EINVAL, "pool k or v is NULL");
   if (pool->n_layers <= 0 || pool->n_slots <= 0 || pool->n_kv_heads <= 0)
     return fail(PKV_ESHAPE, "pool needs n_layers, n_slots, n_kv_heads > 0 (got %lld, %lld, %d)",
@@ -173,6 +177,7 @@ pkv_status decode_prepare(const pkv_kv_pool* pool, int32_t layer, const void* q,
   a->n_groups = 0;
   a->max_members = 0;
   a->n_members = 0;
+  a->kv_scale = pool->dtype == PKV_FP8_E4M3 ? pool->kv_scales + 2 * (int64_t)layer : nullptr;
   return PKV_OK;
 }
 
@@ -212,6 +217,12 @@ pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_ne
   const int es = elem_bytes(pool->dtype);
   const int64_t row_bytes = (int64_t)pool->n_kv_heads * pool->head_dim * es;
   const int64_t layer_bytes = pool->n_slots * row_bytes;
+  if (pool->dtype == PKV_FP8_E4M3)
+    return hip_status(pkv::launch_kv_store_fp8((char*)pool->k + layer * layer_bytes,
+                                               (char*)pool->v + layer * layer_bytes, pool->n_slots,
+                                               row_bytes, k_new, v_new, loc, n_tokens,
+                                               pool->kv_scales + 2 * (int64_t)layer, stream),
+                      "kv_store launch");
   return hip_status(pkv::launch_kv_store((char*)pool->k + layer * layer_bytes,
                                          (char*)pool->v + layer * layer_bytes, pool->n_slots,
                                          row_bytes, k_new, v_new, loc, n_tokens, stream),
@@ -227,6 +238,8 @@ pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void*
   if ((s = check_pool(pool, layer)) != PKV_OK) return s;
   if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens must be >= 0");
   if (n_tokens > (int64_t)1 << 40) return fail(PKV_EINVAL, "n_tokens too large");
+  if (pool->dtype == PKV_FP8_E4M3)
+    return fail(PKV_EUNSUPPORTED, "rope_kv_store supports F32 and BF16 pools");
   if (interleaved != 0 && interleaved != 1) return fail(PKV_EINVAL, "interleaved must be 0 or 1");
   if (max_pos <= 0) return fail(PKV_EINVAL, "max_pos must be > 0");
   if ((q == nullptr) != (q_out == nullptr))

@@ -25,6 +25,27 @@ struct elem_size<bf16_t> {
   static constexpr int value = 2;
 };
 
+// One-byte E4M3 code of an FP8 KV pool (OCP 8-bit floating point, E4M3: bias
+// 7, subnormals, no infinities, largest finite 448).
+struct fp8_t {
+  uint8_t bits;
+};
+template <>
+struct elem_size<fp8_t> {
+  static constexpr int value = 1;
+};
+
+// Element type of q and of the output for a KV storage type: the storage type
+// itself, except bf16 for FP8 pools.
+template <typename T>
+struct io_type {
+  using type = T;
+};
+template <>
+struct io_type<fp8_t> {
+  using type = bf16_t;
+};
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
@@ -42,6 +63,47 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Two E4M3 codes (bytes 2 hi .. 2 hi + 1 of w) widened exactly to a packed
+// bf16 pair (every E4M3 value, subnormals included, is a bf16 value).
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// 16 codes -> 16 bf16 values: codes 0..7 in `a`, codes 8..15 in `b`.
+__device__ __forceinline__ void fp8x16_to_bf16x16(u32x4 c, u32x4& a, u32x4& b) {
+  a = u32x4{fp8x2_to_bf16x2<false>(c[0]), fp8x2_to_bf16x2<true>(c[0]),
+            fp8x2_to_bf16x2<false>(c[1]), fp8x2_to_bf16x2<true>(c[1])};
+  b = u32x4{fp8x2_to_bf16x2<false>(c[2]), fp8x2_to_bf16x2<true>(c[2]),
+            fp8x2_to_bf16x2<false>(c[3]), fp8x2_to_bf16x2<true>(c[3])};
+}
+
+// E4M3 code of the fp32 quotient x / s (correctly rounded division), rounded
+// to nearest even by the conversion; magnitudes beyond 448 saturate (the
+// conversion alone would give NaN there); NaN stays a NaN code.
+__device__ __forceinline__ float fp8_sat_quotient(float x, float s) {
+  const float y = x / s;
+  return fabsf(y) > 448.f ? copysignf(448.f, y) : y;
+}
+__device__ __forceinline__ uint32_t quant_fp8x4(float a, float b, float c, float d, float s) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat_quotient(a, s), fp8_sat_quotient(b, s), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_sat_quotient(c, s), fp8_sat_quotient(d, s), w, true);
+  return (uint32_t)w;
+}
+
+// 16 bf16 values (two 16-byte chunks) -> 16 E4M3 codes under scale s.
+__device__ __forceinline__ u32x4 quant_bf16x16(u32x4 a, u32x4 b, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    r[i] = quant_fp8x4(bf16lo_to_f32(a[2 * i]), bf16hi_to_f32(a[2 * i]),
+                       bf16lo_to_f32(a[2 * i + 1]), bf16hi_to_f32(a[2 * i + 1]), s);
+    r[2 + i] = quant_fp8x4(bf16lo_to_f32(b[2 * i]), bf16hi_to_f32(b[2 * i]),
+                           bf16lo_to_f32(b[2 * i + 1]), bf16hi_to_f32(b[2 * i + 1]), s);
+  }
+  return r;
 }
 
 // dot of two packed bf16 pairs accumulated into fp32 (v_dot2_f32_bf16).

@@ -1,0 +1,14 @@
+// Decode kernel instantiations for FP8 (E4M3) K/V with bf16 q and output,
+// head_dim 64 (one translation unit per variant so the library builds in
+// parallel). Every group size runs the MFMA kernel, with the codes widened to
+// bf16 in registers; the merge is the bf16 one.
+#include "decode_impl.hpp"
+#include "decode_mfma.hpp"
+
+namespace pkv {
+
+hipError_t launch_decode_partials_fp8_64(const DecodeArgs& a, hipStream_t stream) {
+  return decode_mfma::partials_for_dim<64, fp8_t>(a, stream);
+}
+
+}  // namespace pkv

@@ -393,7 +393,8 @@ __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh,
     // a padded request (L = 0) has no split: its rows are zero
     if (c.S == 0 && c.Sp == 0 && s == 0 && a.out)
       for (int i = threadIdx.x; i < G * D; i += NT)
-        store_out<T>(a.out, ((int64_t)b * a.n_q_heads + kvh * G) * D + i, 0.f);
+        store_out<typename io_type<T>::type>(a.out, ((int64_t)b * a.n_q_heads + kvh * G) * D + i,
+                                             0.f);
     return false;
   }
   c.lo = p.P + s * c.chunk;
@@ -406,7 +407,8 @@ __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh,
 }
 
 // Store of the new token (position L-1) of this KV head by the wave whose
-// share [wlo, whi) holds it, completed before that wave reads it back.
+// share [wlo, whi) holds it, completed before that wave reads it back. FP8
+// pools take bf16 rows, quantised under the layer's K or V scale.
 template <typename T, int D>
 __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const SplitCtx& c, int b,
                                                 int kvh, int wlo, int whi, int lane) {
@@ -414,6 +416,21 @@ __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const Split
   if (!a.k_new || c.L - 1 < wlo || c.L - 1 >= whi) return;
   const int raw = c.row[c.L - 1];
   constexpr int CPR = ROW / 16;  // 16-byte chunks of one (slot, KV head) row
+  if constexpr (elem_size<T>::value == 1) {
+    if (raw >= 0 && raw < c.n_slots && lane < 2 * CPR) {
+      const int chk = lane % CPR;
+      const bool is_k = lane < CPR;
+      const char* src = (const char*)(is_k ? a.k_new : a.v_new) +
+                        ((int64_t)b * a.n_kv_heads + kvh) * (2 * ROW) + 32 * chk;
+      char* dst = (char*)(is_k ? a.k : a.v) + (int64_t)raw * c.row_stride + (int64_t)kvh * ROW +
+                  16 * chk;
+      *(u32x4*)dst = quant_bf16x16(*(const u32x4*)src, *(const u32x4*)(src + 16),
+                                   a.kv_scale[is_k ? 0 : 1]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   if (raw >= 0 && raw < c.n_slots && lane < 2 * CPR) {
     const int chk = lane % CPR;
     const char* src = (const char*)(lane < CPR ? a.k_new : a.v_new) +
@@ -454,7 +471,7 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* r
     }
     const float o = num / den;
     if (direct) {
-      store_out<T>(a.out, ((int64_t)b * a.n_q_heads + qh0 + h) * D + d, o);
+      store_out<typename io_type<T>::type>(a.out, ((int64_t)b * a.n_q_heads + qh0 + h) * D + d, o);
       continue;
     }
     const int64_t part = part0 + (int64_t)h * a.split.max_splits + s;

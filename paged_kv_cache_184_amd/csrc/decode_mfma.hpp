@@ -81,10 +81,32 @@ __device__ __forceinline__ u32x2 tr_read(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Per-lane loads of one 32-key block for a KV storage type. bf16: one
+// 16-byte K load per k-step, V in the layout of its LDS tile. FP8 (E4M3
+// codes): one 16-byte K load holds the 16 codes of two k-steps (key row
+// bytes 16 quad + 64 kl .. +15), widened to bf16 before the MFMAs; V chunks
+// are widened to bf16 before they are written to the (bf16) LDS tile.
+template <int D, typename KV>
+struct KVLd;
 template <int D>
+struct KVLd<D, bf16_t> {
+  static constexpr int ROW = 2 * D;        // bytes of one (slot, KV head) row
+  static constexpr int KL = D / 32;        // K loads per key tile
+  static constexpr int NV = MGeo<D>::NI;   // V loads per block
+};
+template <int D>
+struct KVLd<D, fp8_t> {
+  static constexpr int ROW = D;
+  static constexpr int KL = D / 64;
+  static constexpr int CPR = D / 16;       // 16-byte chunks per code row
+  static constexpr int RPI = 64 / CPR;     // rows per wave-wide 1 KiB load
+  static constexpr int NV = kBlk / RPI;
+};
+
+template <int D, typename KV = bf16_t>
 struct KBlock {
-  u32x4 f[2][MGeo<D>::KS];  // K: [key tile][k-step]
-  u32x4 v[MGeo<D>::NI];     // V: this lane's 16 bytes of each 1 KiB row group
+  u32x4 f[2][KVLd<D, KV>::KL];  // K: [key tile][load]
+  u32x4 v[KVLd<D, KV>::NV];     // V: this lane's 16 bytes of each 1 KiB row group
 };
 
 // Per-wave state for NTC column tiles of 16 query rows each.
@@ -110,11 +132,12 @@ __device__ __forceinline__ void init_state(WaveState<D, NTC>& st) {
 // the layout its LDS tile is written in (lane l of row group t holds row
 // RPI t + l / CPR, physical chunk l % CPR). Positions past ce re-read the
 // last valid token.
-template <int D>
-__device__ __forceinline__ void issue_block(KBlock<D>& kb, const int* slots, int i, int cb,
+template <int D, typename KV = bf16_t>
+__device__ __forceinline__ void issue_block(KBlock<D, KV>& kb, const int* slots, int i, int cb,
                                             int ce, const char* kbase, const char* vbase,
                                             int64_t row_stride, int lane) {
   using Gm = MGeo<D>;
+  using Ld = KVLd<D, KV>;
   const int col = lane & 15;
   const int quad = lane >> 4;
   const int last = ce - cb - 1;
@@ -122,33 +145,67 @@ __device__ __forceinline__ void issue_block(KBlock<D>& kb, const int* slots, int
   for (int kt = 0; kt < 2; ++kt) {
     const int64_t off = (int64_t)slots[min(kBlk * i + 16 * kt + col, last)] * row_stride;
 #pragma unroll
-    for (int ks = 0; ks < Gm::KS; ++ks)
-      kb.f[kt][ks] = *(const u32x4*)(kbase + off + 16 * quad + 64 * ks);
+    for (int kl = 0; kl < Ld::KL; ++kl)
+      kb.f[kt][kl] = *(const u32x4*)(kbase + off + 16 * quad + 64 * kl);
   }
-  const int prow = lane / Gm::CPR;
-  const int pch = lane % Gm::CPR;
+  if constexpr (sizeof(KV) == 2) {
+    const int prow = lane / Gm::CPR;
+    const int pch = lane % Gm::CPR;
 #pragma unroll
-  for (int t = 0; t < Gm::NI; ++t) {
-    const int r = Gm::RPI * t + prow;
-    const int lch = pch ^ (r & (Gm::CPR - 1));
-    const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
-    kb.v[t] = *(const u32x4*)(vbase + off + 16 * lch);
+    for (int t = 0; t < Gm::NI; ++t) {
+      const int r = Gm::RPI * t + prow;
+      const int lch = pch ^ (r & (Gm::CPR - 1));
+      const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
+      kb.v[t] = *(const u32x4*)(vbase + off + 16 * lch);
+    }
+  } else {
+    // lane l of load t: row RPI t + l / CPR, code chunk l % CPR
+#pragma unroll
+    for (int t = 0; t < Ld::NV; ++t) {
+      const int r = Ld::RPI * t + lane / Ld::CPR;
+      const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
+      kb.v[t] = *(const u32x4*)(vbase + off + 16 * (lane % Ld::CPR));
+    }
   }
 }
 
-template <int D, int NTC>
-__device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBlock<D>& kb,
+template <int D, int NTC, typename KV = bf16_t>
+__device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBlock<D, KV>& kb,
                                               char* vstage,
                                               const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                               float scale2, int key0, int whi, int lane) {
   using Gm = MGeo<D>;
+  using Ld = KVLd<D, KV>;
   const int col = lane & 15;
   const int quad = lane >> 4;
   // V tile into LDS first (read back transposed below, after the S MFMAs;
   // this wave's earlier reads of the tile precede these writes in LDS order)
+  if constexpr (sizeof(KV) == 2) {
 #pragma unroll
-  for (int t = 0; t < Gm::NI; ++t)
-    *(u32x4*)(vstage + Gm::RPI * t * Gm::ROW + 16 * lane) = kb.v[t];
+    for (int t = 0; t < Gm::NI; ++t)
+      *(u32x4*)(vstage + Gm::RPI * t * Gm::ROW + 16 * lane) = kb.v[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < Ld::NV; ++t) {
+      const int r = Ld::RPI * t + lane / Ld::CPR;
+      const int c = lane % Ld::CPR;  // bf16 chunks 2c, 2c + 1 of row r
+      u32x4 lo, hi;
+      fp8x16_to_bf16x16(kb.v[t], lo, hi);
+      *(u32x4*)(vstage + swz<D>(r, 2 * c)) = lo;
+      *(u32x4*)(vstage + swz<D>(r, 2 * c + 1)) = hi;
+    }
+  }
+  // K fragments as bf16, k-step ks (FP8: widened from half a 16-byte load)
+  u32x4 kf[2][Gm::KS];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int kl = 0; kl < Ld::KL; ++kl) {
+      if constexpr (sizeof(KV) == 2)
+        kf[kt][kl] = kb.f[kt][kl];
+      else
+        fp8x16_to_bf16x16(kb.f[kt][kl], kf[kt][2 * kl], kf[kt][2 * kl + 1]);
+    }
   u32x4 pf[NTC];
 #pragma unroll
   for (int tc = 0; tc < NTC; ++tc) {
@@ -158,7 +215,7 @@ __device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBloc
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < Gm::KS; ++ks) s[kt] = mfma16(kb.f[kt][ks], qf[tc][ks], s[kt]);
+      for (int ks = 0; ks < Gm::KS; ++ks) s[kt] = mfma16(kf[kt][ks], qf[tc][ks], s[kt]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -214,27 +271,27 @@ __device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBloc
 
 // NB consecutive 32-key blocks of one super-block, straight-line: block i's
 // loads are issued one block before its compute, into ring entry i % 2.
-template <int D, int NTC, int NB>
+template <int D, int NTC, int NB, typename KV = bf16_t>
 __device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, const int* slots,
                                           int cb, int ce, const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                           const char* kbase, const char* vbase,
                                           int64_t row_stride, float scale2, int whi, int lane) {
-  KBlock<D> kb[kRing];
-  issue_block<D>(kb[0], slots, 0, cb, ce, kbase, vbase, row_stride, lane);
+  KBlock<D, KV> kb[kRing];
+  issue_block<D, KV>(kb[0], slots, 0, cb, ce, kbase, vbase, row_stride, lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     if (i + 1 < NB)
-      issue_block<D>(kb[(i + 1) % 2], slots, i + 1, cb, ce, kbase, vbase, row_stride, lane);
+      issue_block<D, KV>(kb[(i + 1) % 2], slots, i + 1, cb, ce, kbase, vbase, row_stride, lane);
     // keep the next block's loads ahead of this block's MFMAs
     __builtin_amdgcn_sched_barrier(0);
-    compute_block<D, NTC>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
+    compute_block<D, NTC, KV>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
   }
 }
 
 // A wave's contiguous key range [wlo, whi) of one request row, in 128-key
 // super-blocks: the slot ids of each are staged in this wave's LDS row (the
 // next super-block's prefetched into registers meanwhile).
-template <int D, int NTC>
+template <int D, int NTC, typename KV = bf16_t>
 __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, char* vtile,
                                           const int32_t* row, int n_slots, int wlo, int whi,
                                           const u32x4 (&qf)[NTC][MGeo<D>::KS], const char* kbase,
@@ -260,8 +317,8 @@ __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, cha
     switch (ceil_div(ce - cb, kBlk)) {
 #define PKV_DM_RUN(n)                                                                         \
   case n:                                                                                     \
-    block_run<D, NTC, n>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, whi, \
-                         lane);                                                               \
+    block_run<D, NTC, n, KV>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, \
+                             whi, lane);                                                      \
     break;
       PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
 #undef PKV_DM_RUN
@@ -274,11 +331,12 @@ __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, cha
 // The work of one (KV head kvh, split s, request b) workgroup of kW waves.
 // LDS comes from the caller: the per-wave V tiles vs0 (which also take the
 // waves' merge rows), slot ids slot_lds[kW][kSB * kBlk] and red_ml.
-template <int D, int G>
+template <int D, int G, typename KV = bf16_t>
 __device__ __forceinline__ void mfma_split(const DecodeArgs& a, int kvh, int s, int b,
                                            char (*vs0)[MGeo<D>::VST], int (*slot_lds)[kSB * kBlk],
                                            float (*red_ml)[G][2]) {
   using Gm = MGeo<D>;
+  constexpr bool kFp8 = sizeof(KV) == 1;
   static_assert(G <= 16, "one MFMA column per query head");
   static_assert(G * D * 4 <= Gm::VST, "a wave's merge rows fit in its V tile");
   const int wave = threadIdx.x >> 6;
@@ -287,30 +345,35 @@ __device__ __forceinline__ void mfma_split(const DecodeArgs& a, int kvh, int s, 
   const int quad = lane >> 4;
 
   SplitCtx sc;
-  if (!split_setup<bf16_t, D, G, 64 * kW>(a, b, kvh, s, sc)) return;
+  if (!split_setup<KV, D, G, 64 * kW>(a, b, kvh, s, sc)) return;
   // this wave's contiguous share of the split, a multiple of 32 tokens
   const int sub = ceil_div(ceil_div(sc.hi - sc.lo, kW), kBlk) * kBlk;
   const int wlo = min(sc.hi, sc.lo + wave * sub);
   const int whi = min(sc.hi, wlo + sub);
-  store_new_token<bf16_t, D>(a, sc, b, kvh, wlo, whi, lane);
+  store_new_token<KV, D>(a, sc, b, kvh, wlo, whi, lane);
 
-  const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
-  const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
-  // Q^T fragments (B operand): head col, head_dim 8 quad + 32 ks .. +7; zero
-  // for the columns past the group
+  const char* kbase = (const char*)a.k + (int64_t)kvh * KVLd<D, KV>::ROW;
+  const char* vbase = (const char*)a.v + (int64_t)kvh * KVLd<D, KV>::ROW;
+  // Q^T fragments (B operand), column col = head, zero past the group. k-step
+  // ks holds head_dim 32 ks + 8 quad .. +7 for bf16 K; for FP8 K it holds the
+  // elements the K loads put there: 64 (ks/2) + 16 quad + 8 (ks%2) .. +7.
   const int qh0 = kvh * G;
   u32x4 qf[1][Gm::KS];
-  const char* qp = (const char*)a.q + ((int64_t)b * a.n_q_heads + qh0 + min(col, G - 1)) * Gm::ROW +
-                   16 * quad;
+  const char* qp =
+      (const char*)a.q + ((int64_t)b * a.n_q_heads + qh0 + min(col, G - 1)) * Gm::ROW;
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
-    const u32x4 v = *(const u32x4*)(qp + 64 * ks);
+    const int byte = kFp8 ? 128 * (ks / 2) + 32 * quad + 16 * (ks % 2) : 64 * ks + 16 * quad;
+    const u32x4 v = *(const u32x4*)(qp + byte);
     qf[0][ks] = col < G ? v : u32x4{0u, 0u, 0u, 0u};
   }
+  // FP8: the K scale folds into the softmax scale, the V scale into O
+  const float kscale = kFp8 ? a.kv_scale[0] : 1.f;
+  const float vscale = kFp8 ? a.kv_scale[1] : 1.f;
   WaveState<D, 1> st;
   init_state(st);
-  wave_loop<D, 1>(st, slot_lds[wave], vs0[wave], sc.row, sc.n_slots, wlo, whi, qf, kbase, vbase,
-                  sc.row_stride, a.scale * kLog2e, lane);
+  wave_loop<D, 1, KV>(st, slot_lds[wave], vs0[wave], sc.row, sc.n_slots, wlo, whi, qf, kbase,
+                      vbase, sc.row_stride, a.scale * kLog2e * kscale, lane);
 
   // Hand the wave's (m, l, O) to LDS; an empty wave leaves m = -inf, l = 0, O = 0.
   // The O rows go into this wave's V tile (its transpose reads have returned:
@@ -320,18 +383,18 @@ __device__ __forceinline__ void mfma_split(const DecodeArgs& a, int kvh, int s, 
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[0][dt][r];
+      for (int r = 0; r < 4; ++r)
+        mine[col * D + 16 * dt + 4 * quad + r] = kFp8 ? st.o[0][dt][r] * vscale : st.o[0][dt][r];
     if (quad == 0) {
       red_ml[wave][col][0] = st.m[0];
       red_ml[wave][col][1] = st.lsum[0][0];
     }
   }
   __syncthreads();
-  finish_split<bf16_t, D, G, kW>(a, (const float*)&vs0[0][0], Gm::VST / 4, red_ml, b, kvh, s,
-                                 sc);
+  finish_split<KV, D, G, kW>(a, (const float*)&vs0[0][0], Gm::VST / 4, red_ml, b, kvh, s, sc);
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char vs0[kW][MGeo<D>::VST];
   __shared__ int slot_lds[kW][kSB * kBlk];
@@ -341,16 +404,26 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
     index_step_block<64 * kW>(a, &slot_lds[0][0]);
-  mfma_split<D, G>(a, kvh, s, b, vs0, slot_lds, red_ml);
+  mfma_split<D, G, KV>(a, kvh, s, b, vs0, slot_lds, red_ml);
 }
 
-template <int D>
+// bf16 pools use this kernel for g >= 8 (the VALU kernel takes smaller
+// groups); FP8 pools use it for every group size.
+template <int D, typename KV = bf16_t>
 hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
+  if constexpr (sizeof(KV) == 1) {
+    switch (g) {
+      case 1: decode_mfma_kernel<D, 1, KV><<<grid, 64 * kW, 0, stream>>>(a); return hipGetLastError();
+      case 2: decode_mfma_kernel<D, 2, KV><<<grid, 64 * kW, 0, stream>>>(a); return hipGetLastError();
+      case 4: decode_mfma_kernel<D, 4, KV><<<grid, 64 * kW, 0, stream>>>(a); return hipGetLastError();
+      default: break;
+    }
+  }
   switch (g) {
-    case 8: decode_mfma_kernel<D, 8><<<grid, 64 * kW, 0, stream>>>(a); break;
-    case 16: decode_mfma_kernel<D, 16><<<grid, 64 * kW, 0, stream>>>(a); break;
+    case 8: decode_mfma_kernel<D, 8, KV><<<grid, 64 * kW, 0, stream>>>(a); break;
+    case 16: decode_mfma_kernel<D, 16, KV><<<grid, 64 * kW, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

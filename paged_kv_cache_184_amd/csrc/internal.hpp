@@ -43,6 +43,8 @@ struct DecodeArgs {
   int32_t n_groups;
   int32_t max_members;           // bound on the members of one group
   int32_t n_members;             // length of group_members
+  // FP8 pools: this layer's (k_scale, v_scale); a code c stands for e4m3(c) * scale
+  const float* kv_scale;
 };
 
 // Cascade decode partials: the groups' prefix splits and every request's own
@@ -58,6 +60,11 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
                            const void* k_new, const void* v_new, const int32_t* loc,
                            int64_t n_tokens, hipStream_t stream);
+// FP8 pools: bf16 rows quantised to E4M3 codes (row_bytes = codes per row);
+// kv_scale = this layer's (k_scale, v_scale)
+hipError_t launch_kv_store_fp8(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
+                               const void* k_new, const void* v_new, const int32_t* loc,
+                               int64_t n_tokens, const float* kv_scale, hipStream_t stream);
 
 hipError_t launch_metadata(const pkv_batch_meta& m, int32_t mode, pkv_split_cfg split,
                            int32_t* kv_indptr_out, int32_t* loc_out, int64_t loc_capacity,

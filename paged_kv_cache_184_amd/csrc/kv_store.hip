@@ -33,6 +33,29 @@ __global__ __launch_bounds__(256) void kv_store_kernel(char* __restrict__ k, cha
   *(u32x4*)(v + dst) = b;
 }
 
+// FP8 pools: each thread writes one 16-byte chunk (16 codes) of K and the
+// same chunk of V, quantised from 32 bytes of bf16 input under the layer's
+// K or V scale (kv_scale = this layer's (k_scale, v_scale)).
+__global__ __launch_bounds__(256) void kv_store_fp8_kernel(
+    char* __restrict__ k, char* __restrict__ v, int64_t n_slots, int64_t row_bytes, int64_t chunks,
+    const char* __restrict__ kn, const char* __restrict__ vn, const int32_t* __restrict__ loc,
+    int64_t total, const float* __restrict__ kv_scale) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t t = idx / chunks;
+  const int64_t ch = idx - t * chunks;
+  const int64_t slot = loc[t];
+  if (slot < 0 || slot >= n_slots) return;
+  const int64_t src = 2 * (t * row_bytes + ch * 16);  // bf16 input: two bytes per code
+  const int64_t dst = slot * row_bytes + ch * 16;
+  const float ks = kv_scale[0];
+  const float vs = kv_scale[1];
+  const u32x4 a = quant_bf16x16(*(const u32x4*)(kn + src), *(const u32x4*)(kn + src + 16), ks);
+  const u32x4 b = quant_bf16x16(*(const u32x4*)(vn + src), *(const u32x4*)(vn + src + 16), vs);
+  *(u32x4*)(k + dst) = a;
+  *(u32x4*)(v + dst) = b;
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p16, uint8_t* __restrict__ tail,
                                                    int64_t n16, int64_t ntail) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -64,6 +87,19 @@ hipError_t launch_kv_store(void* k_layer, void* v_layer, int64_t n_slots, int64_
   kv_store_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(
       (char*)k_layer, (char*)v_layer, n_slots, row_bytes, chunks, (const char*)k_new,
       (const char*)v_new, loc, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_store_fp8(void* k_layer, void* v_layer, int64_t n_slots, int64_t row_bytes,
+                               const void* k_new, const void* v_new, const int32_t* loc,
+                               int64_t n_tokens, const float* kv_scale, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t chunks = row_bytes / 16;
+  const int64_t total = n_tokens * chunks;
+  const int64_t blocks = (total + 255) / 256;
+  kv_store_fp8_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(
+      (char*)k_layer, (char*)v_layer, n_slots, row_bytes, chunks, (const char*)k_new,
+      (const char*)v_new, loc, total, kv_scale);
   return hipGetLastError();
 }
 

@@ -53,7 +53,14 @@ def dtype_code(dtype: torch.dtype) -> int:
         return _lib.PKV_BF16
     if dtype == torch.float32:
         return _lib.PKV_F32
-    raise TypeError(f"unsupported dtype {dtype}; use torch.bfloat16 or torch.float32")
+    if dtype in (torch.uint8, torch.float8_e4m3fn):
+        return _lib.PKV_FP8_E4M3  # pools only: one-byte E4M3 codes
+    raise TypeError(f"unsupported dtype {dtype}; use bfloat16, float32 or (pools) E4M3 bytes")
+
+
+def io_dtype(pool_dtype: torch.dtype) -> torch.dtype:
+    """dtype of q, the new K/V rows and the output for a pool dtype."""
+    return torch.bfloat16 if dtype_code(pool_dtype) == _lib.PKV_FP8_E4M3 else pool_dtype
 
 
 def _need(cond: bool, msg: str):
@@ -61,15 +68,23 @@ def _need(cond: bool, msg: str):
         raise ValueError(msg)
 
 
-def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor) -> KVPool:
-    """Descriptor of two contiguous [n_layers, n_slots, n_kv_heads, head_dim] pools."""
+def make_pool(k_pool: torch.Tensor, v_pool: torch.Tensor,
+              kv_scales: Optional[torch.Tensor] = None) -> KVPool:
+    """Descriptor of two contiguous [n_layers, n_slots, n_kv_heads, head_dim] pools.
+    E4M3 pools (uint8 or float8_e4m3fn codes) need kv_scales: a contiguous
+    float32 device tensor [n_layers, 2] of (k_scale, v_scale) per layer."""
     _need(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pools must be equal 4D tensors")
     _need(k_pool.is_contiguous() and v_pool.is_contiguous(), "pools must be contiguous")
     _need(k_pool.dtype == v_pool.dtype, "K and V pools must share a dtype")
     n_layers, n_slots, hkv, d = k_pool.shape
-    pool = KVPool(k_pool.data_ptr(), v_pool.data_ptr(), n_layers, n_slots, hkv, d,
-                  dtype_code(k_pool.dtype), 0)
-    pool._tensors = (k_pool, v_pool)  # the descriptor holds raw pointers: keep them alive
+    code = dtype_code(k_pool.dtype)
+    if code == _lib.PKV_FP8_E4M3:
+        _need(kv_scales is not None and kv_scales.dtype == torch.float32 and
+              kv_scales.is_contiguous() and tuple(kv_scales.shape) == (n_layers, 2),
+              "an E4M3 pool needs kv_scales: contiguous float32 [n_layers, 2]")
+    pool = KVPool(k_pool.data_ptr(), v_pool.data_ptr(), n_layers, n_slots, hkv, d, code, 0,
+                  _ptr(kv_scales) if code == _lib.PKV_FP8_E4M3 else None)
+    pool._tensors = (k_pool, v_pool, kv_scales)  # raw pointers inside: keep them alive
     return pool
 
 
@@ -114,10 +129,12 @@ def abi_version() -> int:
     return lib().pkv_abi_version()
 
 
-def kv_store(k_pool, v_pool, layer: int, k_new, v_new, loc, stream=None) -> None:
-    """pool[layer, loc[t]] = new[t] for K and V (pkv_kv_store)."""
-    pool = make_pool(k_pool, v_pool)
-    _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "dtype mismatch")
+def kv_store(k_pool, v_pool, layer: int, k_new, v_new, loc, stream=None, kv_scales=None) -> None:
+    """pool[layer, loc[t]] = new[t] for K and V (pkv_kv_store); E4M3 pools take
+    bf16 rows and store their codes under the layer's scales."""
+    pool = make_pool(k_pool, v_pool, kv_scales)
+    io = io_dtype(k_pool.dtype)
+    _need(k_new.dtype == io and v_new.dtype == io, "dtype mismatch")
     _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
     _need(loc.dtype == torch.int32 and loc.is_contiguous(), "loc must be contiguous int32")
     n = loc.shape[0]
@@ -194,13 +211,15 @@ def workspace_views(ws: torch.Tensor, batch: int, n_q_heads: int, head_dim: int,
 def _q_check(q, pool: KVPool, batch_rows: int):
     _need(q.is_contiguous(), "q must be contiguous")
     _need(q.dim() == 3 and q.shape[0] == batch_rows and q.shape[2] == pool.head_dim, "q shape")
-    _need(dtype_code(q.dtype) == pool.dtype, "q dtype must match the pools")
+    io = _lib.PKV_BF16 if pool.dtype == _lib.PKV_FP8_E4M3 else pool.dtype
+    _need(dtype_code(q.dtype) == io, "q dtype must match the pools (bf16 for E4M3 pools)")
 
 
 def paged_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float,
-                      split: SplitCfg, workspace: torch.Tensor, out=None, stream=None):
+                      split: SplitCfg, workspace: torch.Tensor, out=None, stream=None,
+                      kv_scales=None):
     """Split-KV paged decode (pkv_paged_decode_attn). q: [B, Hq, D]."""
-    pool = make_pool(k_pool, v_pool)
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     if out is None:
         out = torch.empty_like(q)
@@ -242,14 +261,15 @@ def cascade_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta,
 
 def decode_step(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float, split: SplitCfg,
                 workspace: torch.Tensor, k_new=None, v_new=None, kv_indptr_out=None, loc_out=None,
-                splits_out=None, out=None, stream=None):
+                splits_out=None, out=None, stream=None, kv_scales=None):
     """Index step + store of the new tokens + decode attention in one launch
     (pkv_decode_step). k_new, v_new: [B, Hkv, D] or None."""
-    pool = make_pool(k_pool, v_pool)
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     if k_new is not None:
         _need(k_new.is_contiguous() and v_new is not None and v_new.is_contiguous(), "k_new/v_new")
-        _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "k_new/v_new dtype")
+        io = io_dtype(k_pool.dtype)
+        _need(k_new.dtype == io and v_new.dtype == io, "k_new/v_new dtype")
         _need(k_new.numel() == meta.batch * pool.n_kv_heads * pool.head_dim, "k_new shape")
         _need(v_new.numel() == k_new.numel(), "v_new shape")
     for name, t, n in (("kv_indptr_out", kv_indptr_out, meta.batch + 1),
@@ -267,8 +287,8 @@ def decode_step(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float, sp
 
 
 def decode_partials(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float,
-                    split: SplitCfg, workspace: torch.Tensor, stream=None) -> None:
-    pool = make_pool(k_pool, v_pool)
+                    split: SplitCfg, workspace: torch.Tensor, stream=None, kv_scales=None) -> None:
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     _check(lib().pkv_decode_partials(C.byref(pool), layer, q.data_ptr(), q.shape[1],
                                      C.byref(meta), scale, split, workspace.data_ptr(),
@@ -323,8 +343,8 @@ class PreparedCall:
 
 
 def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, workspace, out,
-                   stream=None, stage="all"):
-    pool = make_pool(k_pool, v_pool)
+                   stream=None, stage="all", kv_scales=None):
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     s = None
     if stage == "all":
@@ -336,7 +356,8 @@ def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, work
                             C.byref(meta), scale, split, workspace.data_ptr(), workspace.numel(), s,
                             keep=(pool, meta), stream=stream)
     if stage == "merge":
-        return PreparedCall("pkv_decode_merge", C.byref(meta), q.shape[1], pool.head_dim, pool.dtype,
+        return PreparedCall("pkv_decode_merge", C.byref(meta), q.shape[1], pool.head_dim,
+                            dtype_code(q.dtype),
                             split, workspace.data_ptr(), workspace.numel(), out.data_ptr(), s,
                             keep=(pool, meta), stream=stream)
     raise ValueError(stage)
@@ -344,8 +365,8 @@ def prepare_decode(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, work
 
 def prepare_decode_step(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split, workspace, out,
                         k_new=None, v_new=None, kv_indptr_out=None, loc_out=None,
-                        splits_out=None, stream=None):
-    pool = make_pool(k_pool, v_pool)
+                        splits_out=None, stream=None, kv_scales=None):
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     return PreparedCall("pkv_decode_step", C.byref(pool), layer, q.data_ptr(), _ptr(k_new),
                         _ptr(v_new), q.shape[1], C.byref(meta), scale, split,
@@ -363,8 +384,8 @@ def prepare_cascade_decode(q, k_pool, v_pool, layer, meta: BatchMeta, groups, sc
                         stream=stream)
 
 
-def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None):
-    pool = make_pool(k_pool, v_pool)
+def prepare_kv_store(k_pool, v_pool, layer, k_new, v_new, loc, stream=None, kv_scales=None):
+    pool = make_pool(k_pool, v_pool, kv_scales)
     return PreparedCall("pkv_kv_store", C.byref(pool), layer, k_new.data_ptr(), v_new.data_ptr(),
                         loc.data_ptr(), loc.shape[0], None, keep=(pool,), stream=stream)
 

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_info_calls(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == _lib.PKV_ABI_VERSION == 2
     assert lib.pkv_status_str(_lib.PKV_EWORKSPACE) == b"PKV_EWORKSPACE"
     assert lib.pkv_status_str(99) == b"PKV_UNKNOWN"
 
@@ -158,6 +158,35 @@ def test_rope_kv_store_rejects(lib):
     assert call(q=None, q_out=None, k=None, v=None, pos=None, tab=None, loc=None,
                 n=0) == _lib.PKV_OK
     assert lib.pkv_last_error() == b""
+
+
+def test_fp8_pool_rules(lib):
+    """E4M3 pools need 8-byte aligned kv_scales; rope_kv_store, prefill and
+    cascade decode reject them; the merge's dtype is the output's (F32/BF16).
+    Only error paths are called: nothing is launched."""
+    fp8 = _lib.PKV_FP8_E4M3
+    store = lib.pkv_kv_store
+    assert store(C.byref(_pool(dtype=fp8)), 0, 16, 16, 16, 1, None) == _lib.PKV_EINVAL
+    assert store(C.byref(_pool(dtype=fp8, kv_scales=68)), 0, 16, 16, 16, 1, None) == _lib.PKV_EINVAL
+    assert b"kv_scales" in lib.pkv_last_error()
+    ok_pool = _pool(dtype=fp8, kv_scales=64)
+    assert store(C.byref(ok_pool), 0, 24, 16, 16, 1, None) == _lib.PKV_EALIGN
+    assert store(C.byref(ok_pool), 0, 16, 16, 16, 0, None) == _lib.PKV_OK  # no-op
+    assert lib.pkv_rope_kv_store(C.byref(ok_pool), 0, None, None, 0, 16, 16, 16, 8, 4, 1, 16, 1,
+                                 None) == _lib.PKV_EUNSUPPORTED
+    meta = _meta()
+    meta_qo = _meta(qo_indptr=64)
+    assert lib.pkv_paged_prefill_attn(C.byref(ok_pool), 0, 16, 4, C.byref(meta_qo), 1, 1, 0.125,
+                                      1, 16, None) == _lib.PKV_EUNSUPPORTED
+    groups = _lib.PrefixGroups(16, 32, 48, 1, 2, 2, 0)
+    assert lib.pkv_cascade_decode_attn(C.byref(ok_pool), 0, 16, 4, C.byref(meta), C.byref(groups),
+                                       0.125, _split(), 256, 1 << 20, 16,
+                                       None) == _lib.PKV_EUNSUPPORTED
+    assert lib.pkv_decode_merge(C.byref(meta), 4, 64, fp8, _split(), 256, 1 << 20, 16,
+                                None) == _lib.PKV_EDTYPE
+    # decode with a missing scale table is refused before any launch
+    assert lib.pkv_paged_decode_attn(C.byref(_pool(dtype=fp8)), 0, 16, 4, C.byref(meta), 0.125,
+                                     _split(), 256, 1 << 20, 16, None) == _lib.PKV_EINVAL
 
 
 def _decode(lib, pool=None, layer=0, q=16, hq=4, meta=None, scale=0.125, split=None, ws=256,
