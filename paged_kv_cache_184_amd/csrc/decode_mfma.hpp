@@ -270,21 +270,25 @@ __device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBloc
 }
 
 // NB consecutive 32-key blocks of one super-block, straight-line: block i's
-// loads are issued one block before its compute, into ring entry i % 2.
+// loads are issued kRing - 1 blocks before its compute, into ring entry
+// i % kRing.
 template <int D, int NTC, int NB, typename KV = bf16_t>
 __device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, const int* slots,
                                           int cb, int ce, const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                           const char* kbase, const char* vbase,
                                           int64_t row_stride, float scale2, int whi, int lane) {
   KBlock<D, KV> kb[kRing];
-  issue_block<D, KV>(kb[0], slots, 0, cb, ce, kbase, vbase, row_stride, lane);
+#pragma unroll
+  for (int j = 0; j < kRing - 1; ++j)
+    if (j < NB) issue_block<D, KV>(kb[j], slots, j, cb, ce, kbase, vbase, row_stride, lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    if (i + 1 < NB)
-      issue_block<D, KV>(kb[(i + 1) % 2], slots, i + 1, cb, ce, kbase, vbase, row_stride, lane);
-    // keep the next block's loads ahead of this block's MFMAs
+    if (i + kRing - 1 < NB)
+      issue_block<D, KV>(kb[(i + kRing - 1) % kRing], slots, i + kRing - 1, cb, ce, kbase, vbase,
+                         row_stride, lane);
+    // keep the later blocks' loads ahead of this block's MFMAs
     __builtin_amdgcn_sched_barrier(0);
-    compute_block<D, NTC, KV>(st, kb[i % 2], vstage, qf, scale2, cb + kBlk * i, whi, lane);
+    compute_block<D, NTC, KV>(st, kb[i % kRing], vstage, qf, scale2, cb + kBlk * i, whi, lane);
   }
 }
 
@@ -315,12 +319,14 @@ __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, cha
       for (int j = 0; j < SBK / 64; ++j) ids[j] = row[min(nb + lane + 64 * j, whi - 1)];
     }
     switch (ceil_div(ce - cb, kBlk)) {
-#define PKV_DM_RUN(n)                                                                         \
-  case n:                                                                                     \
-    block_run<D, NTC, n, KV>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, \
-                             whi, lane);                                                      \
+#define PKV_DM_RUN(n)                                                                          \
+  case n:                                                                                      \
+    if constexpr (n <= kSB)                                                                    \
+      block_run<D, NTC, n, KV>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, \
+                               whi, lane);                                                     \
     break;
       PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
+      PKV_DM_RUN(5) PKV_DM_RUN(6) PKV_DM_RUN(7) PKV_DM_RUN(8)
 #undef PKV_DM_RUN
       default: break;
     }
