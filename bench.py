@@ -429,14 +429,17 @@ KERNEL_SOURCES = ["paged_kv_cache_184_amd/csrc/decode_impl.hpp",
                   "paged_kv_cache_184_amd/csrc/internal.hpp"]
 
 
-def measured_traffic():
+def measured_traffic(alg_bytes: int):
     """HBM bytes per launch of the partial kernel from the committed counter
-    runs, or None when the kernel sources changed since they were taken."""
+    runs, or None when the kernel sources changed since they were taken or the
+    counters were taken on another workload (other algorithmic bytes)."""
     import hashlib
 
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
+        if int(rec["alg_bytes"]) != int(alg_bytes):
+            return None
         h = hashlib.sha256()
         for rel in KERNEL_SOURCES:
             with open(os.path.join(ROOT, rel), "rb") as f:
@@ -626,7 +629,7 @@ def main():
         "host_s_timed_region": round(host_s, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "traffic_unit": "bytes per launch",
+                     "traffic": measured_traffic(db.partial_kernel_bytes()), "traffic_unit": "bytes per launch",
                      "algorithmic_bytes_per_launch": db.partial_kernel_bytes(),
                      "kernel": "decode_partial_kernel<bf16,128,4>"},
         "detail": detail,

@@ -39,13 +39,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-file flags. prefill.hip: -fno-honor-nans drops the quieting max(x, x)
+# that IEEE min/max semantics would put before every row-maximum step on the
+# MFMA scores (a third of the softmax VALU work); the kernel reads only valid
+# slots, takes a finite scale (checked by the API) and masks with -inf, so no
+# NaN reaches those maxima.
+FILE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(hipcc, src, extra):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *CFLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; drop that line
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

@@ -40,6 +40,8 @@
 // masked. Tiles are issued longest-first (highest token offset first).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -111,11 +113,13 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 // with m = the exact row maxima, collected in mseen). With kTau = 64 the
 // weights stay below 2^64, so P, the row sums and O stay far from the fp32 /
 // bf16 range limit until `bad` is raised.
-template <int D, int G>
+// MASK: the block straddles the causal diagonal or the sequence end (a
+// separate instantiation, so unmasked blocks carry no per-score selects).
+template <int D, int G, bool MASK>
 __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
     const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
-    float (&m)[2], float (&mseen)[2], bool& bad, bool init, bool mask, int k0,
+    float (&m)[2], float (&mseen)[2], bool& bad, bool init, int k0,
     const int (&limit)[2], float scale2, int lane) {
   using Gm = PGeo<D>;
   constexpr int KS = Gm::KSTEPS;
@@ -123,10 +127,8 @@ __device__ __forceinline__ void attend_block(
   const int quad = lane >> 4;
   const int s4 = col & 3;
   const u32x4 ones = u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // S^T for key tiles 2j, 2j+1 x 2 query tiles
-    f32x4 s[2][2];
+  // S^T for key tiles 2j, 2j+1 x 2 query tiles
+  auto scores = [&](int j, f32x4 (&s)[2][2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kt = 2 * j + h;
@@ -139,18 +141,31 @@ __device__ __forceinline__ void attend_block(
         s[h][1] = mfma16(ka, qf[1][ks], s[h][1]);
       }
     }
+  };
+  // Both halves' S MFMAs are issued first: the second half's run while the
+  // first half's softmax occupies the VALU, and the first half's P.V MFMAs
+  // run while the second half's softmax does. (Interleaving the two with
+  // scheduling groups was measured slower.)
+  f32x4 sc[2][2][2];
+  scores(0, sc[0]);
+  scores(1, sc[1]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f32x4 (&s)[2][2] = sc[j];
     // mask (blocks on the causal diagonal or the sequence end only), then the
     // stabiliser check on the raw maxima
-    if (mask) {
+    if constexpr (MASK) {
+      // key k0 + 32 j + 4 quad + (16 h + r) is visible to row tile n when
+      // 16 h + r <= rel[n]: one register per tile, immediates per element
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < 2; ++n) {
+        const int rel = limit[n] - (k0 + 32 * j + 4 * quad);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + 32 * j + 16 * h + 4 * quad + r;
-            s[h][n][r] = key <= limit[n] ? s[h][n][r] : -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r) s[h][n][r] = 16 * h + r <= rel ? s[h][n][r] : -INFINITY;
+      }
     }
     float mx[2];
 #pragma unroll
@@ -209,6 +224,9 @@ __device__ __forceinline__ void attend_block(
       o[dt][0] = mfma16(va, pf[0], o[dt][0]);
       o[dt][1] = mfma16(va, pf[1], o[dt][1]);
     }
+    // keep the two halves apart: hoisting the second half's LDS reads above
+    // the first half's MFMAs would raise the register count past 256
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -356,24 +374,33 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     offsets(0, off);
     issue(0, off);
 
-    for (int i0 = 0; i0 < nblk; i0 += kStages) {
+    // One block: wait for its transfers, queue the next ones, attend.
+    auto block = [&](int i, int u, auto masked) {
+      load_ids(i + 2, u);  // ring u held the ids of block i, already consumed
+      __builtin_amdgcn_s_waitcnt(PKV_VMCNT(1));  // S(i+1) and D(i) landed (this wave)
+      __builtin_amdgcn_s_barrier();              // ... for every wave; block i-1 is done
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      offsets(u ^ 1, off);
+      issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
+      const char* st = stage_ptr(u);
+      attend_block<D, G, decltype(masked)::value>(st, st + Gm::TILE, qf, o, lacc, m, mseen, bad,
+                                                  first_pass && i == 0, i * kBK, limit, scale2,
+                                                  lane);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    };
+    // Blocks that every row sees whole and that end inside the sequence need
+    // no mask; they run in a loop of their own (an even count, so the ring
+    // stages stay compile-time), the rest (the diagonal and the end) after it.
+    const int nfull = min(nblk, min(kv_full, L) / kBK) & ~(kStages - 1);
+    for (int i0 = 0; i0 < nfull; i0 += kStages) {
+      block(i0, 0, std::false_type{});
+      block(i0 + 1, 1, std::false_type{});
+    }
+    for (int i0 = nfull; i0 < nblk; i0 += kStages) {
 #pragma unroll
       for (int u = 0; u < kStages; ++u) {
-        const int i = i0 + u;
-        if (i >= nblk) break;
-        load_ids(i + 2, u);  // ring u held the ids of block i, already consumed
-        __builtin_amdgcn_s_waitcnt(PKV_VMCNT(1));  // S(i+1) and D(i) landed (this wave)
-        __builtin_amdgcn_s_barrier();              // ... for every wave; block i-1 is done
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        offsets(u ^ 1, off);
-        issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
-        const char* st = stage_ptr(u);
-        const int k0 = i * kBK;
-        const bool init = first_pass && i == 0;
-        const bool mask = k0 + kBK > kv_full || k0 + kBK > L;
-        attend_block<D, G>(st, st + Gm::TILE, qf, o, lacc, m, mseen, bad, init, mask, k0, limit,
-                           scale2, lane);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (i0 + u >= nblk) break;
+        block(i0 + u, u, std::true_type{});
       }
     }
     // drain the transfers still in flight (before a second pass or the exit)
