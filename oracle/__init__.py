@@ -42,4 +42,5 @@ from .fp8_kv import (  # noqa: F401
     dequantize,
     kv_store_fp8,
     decode_attention_fp8,
+    prefill_attention_fp8,
 )

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import decode_attention
+from .paged_attention import decode_attention, prefill_attention
 
 E4M3_MAX = 448.0  # R17: 0x7E = 2^8 * (1 + 6/8)
 
@@ -96,3 +96,14 @@ def decode_attention_fp8(q, k_codes, v_codes, kv_scales, layer, req_to_token, re
     kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)
     vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)
     return decode_attention(q, kp, vp, 0, req_to_token, req_pool_indices, seq_lens, scale)
+
+
+def prefill_attention_fp8(q, k_codes, v_codes, kv_scales, layer, req_to_token, req_pool_indices,
+                          seq_lens, qo_indptr, scale, causal=True):
+    """Packed prefill over code pools: the prefill definition on the
+    represented values e4m3(c) * scale of the layer (R20)."""
+    ks, vs = np.asarray(kv_scales, np.float32)[layer]
+    kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)
+    vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)
+    return prefill_attention(q, kp, vp, 0, req_to_token, req_pool_indices, seq_lens, qo_indptr,
+                             scale, causal=causal)

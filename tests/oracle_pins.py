@@ -596,6 +596,31 @@ def pin_decode_fp8_library(O, seed=33):
         np.testing.assert_allclose(out[i], ref, rtol=0, atol=1e-12)
 
 
+def pin_prefill_fp8_library(O, seed=34):
+    """Packed prefill over code pools equals torch SDPA (fp64, causal mask)
+    over K/V dequantised by torch."""
+    lens = np.array([30, 9, 21])
+    n_new = np.array([6, 9, 1])
+    b, v = small_batch(seed, B=3, hq=4, hkv=2, d=16, lens=lens, n_new=n_new)
+    rng = np.random.default_rng(seed)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    kc = rng.choice(finite, size=v.k_pool.shape).astype(np.uint8)
+    vc = rng.choice(finite, size=v.v_pool.shape).astype(np.uint8)
+    scales = np.float32([[0.03, 0.4], [0.01, 0.2]])
+    out = O.prefill_attention_fp8(v.q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
+                                  b.seq_lens, b.qo_indptr, b.scale)
+    for i in range(b.batch):
+        lo, hi = int(b.qo_indptr[i]), int(b.qo_indptr[i + 1])
+        L = int(b.seq_lens[i])
+        n = hi - lo
+        slots = b.req_to_token[b.req_pool_indices[i], :L]
+        K = _torch_fp8_decode(kc[0, slots]) * float(scales[0, 0])
+        V = _torch_fp8_decode(vc[0, slots]) * float(scales[0, 1])
+        mask = np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None]
+        ref = sdpa_reference(v.q[lo:hi], K, V, b.scale, b.group, mask)
+        np.testing.assert_allclose(out[lo:hi], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_decode_vs_sdpa, pin_prefill_vs_sdpa, pin_golden_two_keys, pin_golden_prefill,
     pin_closed_forms, pin_gqa_mapping, pin_slot_permutation, pin_split_merge,
@@ -605,5 +630,5 @@ ALL_PINS = [
     pin_rope_complex, pin_rope_half_split_is_permuted_interleaved, pin_rope_standard_table,
     pin_rope_kv_store, pin_e4m3_decode_library, pin_e4m3_spec_values, pin_e4m3_encode_library,
     pin_e4m3_saturation_and_nan, pin_quantize_fp32_quotient, pin_kv_store_fp8,
-    pin_decode_fp8_library,
+    pin_decode_fp8_library, pin_prefill_fp8_library,
 ]

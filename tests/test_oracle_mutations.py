@@ -78,6 +78,9 @@ FP8_MUTATIONS = {
                                    "vp = dequantize(np.asarray(v_codes)[layer:layer + 1], 1.0)"),
     "decode_fp8_k_scale_for_v": ("kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)",
                                  "kp = dequantize(np.asarray(k_codes)[layer:layer + 1], vs)"),
+    "prefill_fp8_ignores_v_scale": ("vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)\n    return prefill_attention",
+                                    "vp = dequantize(np.asarray(v_codes)[layer:layer + 1], 1.0)\n    return prefill_attention"),
+    "prefill_fp8_not_causal": ("scale, causal=causal)", "scale, causal=False)"),
     "decode_fp8_layer0": ("kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)",
                           "kp = dequantize(np.asarray(k_codes)[0:1], ks)"),
 }
@@ -94,7 +97,8 @@ def mutated_oracle(old, new, target=None):
     assert texts[target].count(old) >= 1, f"mutation anchor not found: {old!r}"
     texts[target] = texts[target].replace(old, new)
     # the FP8 module's relative import resolves to the (possibly mutated) namespace
-    texts[SRC_FP8] = texts[SRC_FP8].replace("from .paged_attention import decode_attention\n", "")
+    texts[SRC_FP8] = "\n".join(l for l in texts[SRC_FP8].split("\n")
+                               if not l.startswith("from .paged_attention import"))
     mod = types.ModuleType("oracle_mutant")
     exec(compile(texts[SRC], "oracle_mutant", "exec"), mod.__dict__)
     exec(compile(texts[SRC_FP8], "oracle_mutant_fp8", "exec"), mod.__dict__)
