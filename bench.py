@@ -346,9 +346,11 @@ class PrefillBench:
     """Packed ragged paged prefill: 8 requests, 64..2048 new tokens each over a
     0..4096-token cached prefix, 32 q / 8 KV heads, head_dim 128, bf16, causal.
     A step is the index step (new-token locations), the store of the new
-    tokens' K/V and the MFMA prefill kernel, rotating over 8 layers."""
+    tokens' K/V and the MFMA prefill kernel, rotating over 8 layers. kv="fp8":
+    E4M3 pools (N(0,1) values under a scale of 1/64, saturated) and a
+    quantising store."""
 
-    def __init__(self, n_layers: int, seed: int):
+    def __init__(self, n_layers: int, seed: int, kv: str = "bf16"):
         import torch
 
         from paged_kv_cache_184_amd import ops
@@ -361,15 +363,22 @@ class PrefillBench:
         g = torch.Generator(device=dev)
         g.manual_seed(seed)
         shape = (b.n_layers, b.n_slots, b.n_kv_heads, b.head_dim)
-        self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
-        self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
         live = torch.from_numpy(b.live_slots).to(dev).long()
-        kv = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
-        kv = kv.to(torch.bfloat16)
+        vals = torch.randn((2, live.numel(), b.n_kv_heads, b.head_dim), generator=g, device=dev)
+        if kv == "fp8":
+            self.kv_scales = torch.full((b.n_layers, 2), 1.0 / 64, dtype=torch.float32, device=dev)
+            self.k_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)  # NaN codes
+            self.v_pool = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+            vals = (vals * 64).clamp_(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            self.kv_scales = None
+            self.k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+            self.v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+            vals = vals.to(torch.bfloat16)
         for layer in range(b.n_layers):
-            self.k_pool[layer, live] = kv[0]
-            self.v_pool[layer, live] = kv[1]
-        del kv
+            self.k_pool[layer, live] = vals[0]
+            self.v_pool[layer, live] = vals[1]
+        del vals
         T = b.total_q
         self.q = torch.randn((T, b.n_q_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
         self.k_new = torch.randn((T, b.n_kv_heads, b.head_dim), generator=g, device=dev).to(torch.bfloat16)
@@ -386,9 +395,10 @@ class PrefillBench:
             self.calls.append((
                 ops.prepare_metadata(self.meta, ops.PKV_MODE_PREFILL, None, None, self.loc, None),
                 ops.prepare_kv_store(self.k_pool, self.v_pool, layer, self.k_new, self.v_new,
-                                     self.loc),
+                                     self.loc, kv_scales=self.kv_scales),
                 ops.prepare_prefill(self.q, self.k_pool, self.v_pool, layer, self.meta,
-                                    b.max_q_len, b.scale, True, self.out),
+                                    b.max_q_len, b.scale, True, self.out,
+                                    kv_scales=self.kv_scales),
             ))
 
     def flops(self) -> float:
@@ -601,6 +611,17 @@ def main():
         print(f"# prefill: {detail['prefill']}", file=sys.stderr, flush=True)
         del pb
         torch.cuda.empty_cache()
+        if not args.no_fp8:
+            pb = PrefillBench(n_layers=8, seed=184_024, kv="fp8")
+            p8_step, p8_attn = pb.run(max(10, args.steps // 5), 3)
+            detail["prefill_fp8"] = {
+                "workload": "packed_prefill (8 requests, T_q=%d), E4M3 pools" % pb.b.total_q,
+                "us_per_step": round(p8_step * 1e3, 1), "kernel_us": round(p8_attn * 1e3, 1),
+                "tflops": round(pb.flops() / (p8_attn * 1e-3) / 1e12, 1),
+                "kernel_vs_bf16": round(p_attn / p8_attn, 3)}
+            print(f"# prefill fp8: {detail['prefill_fp8']}", file=sys.stderr, flush=True)
+            del pb
+            torch.cuda.empty_cache()
     if head is None:
         raise SystemExit("--headline must be one of --ctx")
     db, step_ms, part_ms, host_s = head

@@ -31,8 +31,8 @@
  * always fp32; prefill is BF16 only), head_dim 64 or 128, group size
  * n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}. FP8_E4M3 pools (one-byte codes
  * with per-layer K and V scales, see pkv_kv_pool) hold K/V for the decode
- * entry points and pkv_kv_store; there q, the new K/V rows and the output are
- * BF16 (P4, bullet on the fp8 MMA test kernel of the attention kernels; the
+ * and prefill entry points and pkv_kv_store; there q, the new K/V rows and the
+ * output are BF16 (P4, bullet on the fp8 MMA test kernel of the attention kernels; the
  * code format is the OCP 8-bit floating point E4M3 encoding).
  *
  * Memory safety: kernels clamp every device-supplied index to the buffer it
@@ -320,8 +320,10 @@ pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32
  * start into one forward; P1, bullet on cached prefix pages). The new tokens'
  * K/V must already be stored (pkv_kv_store). q, out: device
  * [total_q, n_q_heads, head_dim], 16-byte aligned. max_q_len >= every n_b sizes
- * the grid (rows i >= max_q_len are not computed). BF16 pools only (any other
- * dtype, FP8_E4M3 included, returns PKV_EUNSUPPORTED): QK^T and PV run on bf16 MFMA with fp32
+ * the grid (rows i >= max_q_len are not computed). BF16 or FP8_E4M3 pools
+ * (F32 returns PKV_EUNSUPPORTED; for FP8_E4M3, q and out are BF16 and the
+ * codes are widened exactly to bf16, the K scale joining the softmax scale and
+ * the V scale the output): QK^T and PV run on bf16 MFMA with fp32
  * accumulation, P is rounded to bf16 for PV and the row sums use those rounded
  * values; any finite scale, including 0 and negative values. Bit-identical run
  * to run and independent of where the slots sit in the pool. */

@@ -452,9 +452,9 @@ pkv_status pkv_paged_prefill_attn(const pkv_kv_pool* pool, int32_t layer, const 
   if (meta->batch == 0 || total_q == 0 || max_q_len == 0) return ok();
   if (!q || !out) return fail(PKV_EINVAL, "q and out are required");
   if (!aligned16(q) || !aligned16(out)) return fail(PKV_EALIGN, "q / out must be 16-byte aligned");
-  if (pool->dtype != PKV_BF16)
-    return fail(PKV_EUNSUPPORTED, "prefill supports BF16 only (MFMA path)");
-  pkv::PrefillArgs a;
+  if (pool->dtype != PKV_BF16 && pool->dtype != PKV_FP8_E4M3)
+    return fail(PKV_EUNSUPPORTED, "prefill supports BF16 and FP8_E4M3 pools (MFMA path)");
+  pkv::PrefillArgs a{};
   const int64_t layer_elems = pool->n_slots * pool->n_kv_heads * pool->head_dim;
   const int es = elem_bytes(pool->dtype);
   a.k = (const char*)pool->k + (int64_t)layer * layer_elems * es;
@@ -477,6 +477,7 @@ pkv_status pkv_paged_prefill_attn(const pkv_kv_pool* pool, int32_t layer, const 
   a.scale = scale;
   a.causal = causal;
   a.out = out;
+  a.kv_scale = pool->dtype == PKV_FP8_E4M3 ? pool->kv_scales + 2 * (int64_t)layer : nullptr;
   return hip_status(pkv::launch_prefill(a, stream), "prefill launch");
 }
 

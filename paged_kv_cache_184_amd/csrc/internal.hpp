@@ -91,6 +91,7 @@ struct PrefillArgs {
   float scale;
   int32_t causal;
   void* out;
+  const float* kv_scale;  // E4M3 pools: this layer's (k_scale, v_scale)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

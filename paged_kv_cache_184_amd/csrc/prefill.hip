@@ -72,8 +72,36 @@ struct PGeo {
   static constexpr int DT = D / 16;              // 16-wide output tiles over head_dim
 };
 
+// Storage side of a K/V row for a pool type: bf16 rows (K and V both by
+// direct-to-LDS transfers), or E4M3 code rows (K by direct-to-LDS transfers
+// into a code tile; V through registers, widened to bf16 and written into the
+// bf16 V tile, so the P.V path is the same for both).
+template <int D, typename KV>
+struct PStore {
+  static constexpr int ROW = D * (int)sizeof(KV);  // bytes of a (slot, KV head) row
+  static constexpr int CPR = ROW / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;             // rows per wave-wide 1 KiB transfer
+  static constexpr int NI = (kBK / 4) / RPI;       // transfers per wave per tile
+  static constexpr int KTILE = kBK * ROW;          // bytes of the K tile
+  static constexpr int STAGE = KTILE + PGeo<D>::TILE;  // K tile + bf16 V tile
+  // code rows: rows sharing one 256-byte bank line, for the K-tile swizzle
+  static constexpr int RPL = ROW >= 256 ? 1 : 256 / ROW;
+};
+
+// Byte offset of logical 16-byte chunk c of row r in a K code tile. Each
+// group of 16 consecutive rows read at one chunk position hits 16 distinct
+// 16-byte bank groups (rows sharing a 256-byte bank line differ in r % RPL,
+// the XOR by r / RPL separates the rest).
+template <int D>
+__device__ __forceinline__ int swz8(int r, int c) {
+  using S = PStore<D, fp8_t>;
+  return r * S::ROW + 16 * (c ^ ((r / S::RPL) & (S::CPR - 1)));
+}
+
 // vmcnt(n) alone (expcnt, lgkmcnt left at their maxima), gfx9 encoding
 #define PKV_VMCNT(n) ((((n) & 15)) | (7 << 4) | (15 << 8) | ((((n) >> 4) & 3) << 14))
+// lgkmcnt(0) alone (vmcnt, expcnt left at their maxima)
+#define PKV_LGKMCNT0 (15 | (7 << 4) | (0 << 8) | (3 << 14))
 
 #define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define PKV_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -115,7 +143,7 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 // bf16 range limit until `bad` is raised.
 // MASK: the block straddles the causal diagonal or the sequence end (a
 // separate instantiation, so unmasked blocks carry no per-score selects).
-template <int D, int G, bool MASK>
+template <int D, int G, bool MASK, typename KV>
 __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
     const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
@@ -134,11 +162,27 @@ __device__ __forceinline__ void attend_block(
       const int kt = 2 * j + h;
       s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
       s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (sizeof(KV) == 2) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 ka = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
-        s[h][0] = mfma16(ka, qf[0][ks], s[h][0]);
-        s[h][1] = mfma16(ka, qf[1][ks], s[h][1]);
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 ka = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
+          s[h][0] = mfma16(ka, qf[0][ks], s[h][0]);
+          s[h][1] = mfma16(ka, qf[1][ks], s[h][1]);
+        }
+      } else {
+        // E4M3 codes: one 16-byte read holds key row bytes 16 quad + 64 kp ..
+        // +15, the elements of k-steps 2 kp (first 8) and 2 kp + 1, widened
+        // exactly to bf16 (the Q fragments are loaded in the same order)
+#pragma unroll
+        for (int kp = 0; kp < KS / 2; ++kp) {
+          u32x4 k0, k1;
+          fp8x16_to_bf16x16(*(const u32x4*)(lds_k + swz8<D>(16 * kt + col, quad + 4 * kp)), k0,
+                            k1);
+          s[h][0] = mfma16(k0, qf[0][2 * kp], s[h][0]);
+          s[h][1] = mfma16(k0, qf[1][2 * kp], s[h][1]);
+          s[h][0] = mfma16(k1, qf[0][2 * kp + 1], s[h][0]);
+          s[h][1] = mfma16(k1, qf[1][2 * kp + 1], s[h][1]);
+        }
       }
     }
   };
@@ -230,15 +274,17 @@ __device__ __forceinline__ void attend_block(
   }
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Gm = PGeo<D>;
+  using Sg = PStore<D, KV>;
+  constexpr bool kFp8 = sizeof(KV) == 1;
   constexpr int BQ = kRows / G;  // tokens per tile
   // One LDS object per ring stage (tiles and slot ids), selected with
   // compile-time indices, so reads of one stage are not ordered behind the
   // transfers into another.
-  __shared__ __attribute__((aligned(1024))) char st0[Gm::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Gm::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st0[Sg::STAGE];  // K tile, then the bf16 V tile
+  __shared__ __attribute__((aligned(1024))) char st1[Sg::STAGE];
   __shared__ __attribute__((aligned(16))) int id0[4][kBK];  // [wave][row]
   __shared__ __attribute__((aligned(16))) int id1[4][kBK];
   __shared__ int redo[4];  // per wave: a score rose past the stabiliser's headroom
@@ -268,16 +314,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
   const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
   const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
-  const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
+  const int64_t row_stride = (int64_t)a.n_kv_heads * Sg::ROW;
 
   // This lane's transfer rows and logical chunk: transfer i of this wave
   // covers tile rows 16*wave + RPI*i .. +RPI-1; lane l lands at physical chunk
   // l % CPR of row 16*wave + RPI*i + l / CPR, so it fetches the logical chunk
   // that the swizzle puts there.
-  const int prow = lane / Gm::CPR;
-  const int pch = lane % Gm::CPR;
-  const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
-  const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
+  const int prow = lane / Sg::CPR;
+  const int pch = lane % Sg::CPR;
+  const char* kbase = (const char*)a.k + (int64_t)kvh * Sg::ROW;
+  const char* vbase = (const char*)a.v + (int64_t)kvh * Sg::ROW;
 
   // Slot ids of a block arrive by DMA too (one 4-byte transfer per lane into a
   // per-wave ring in LDS), so every vector-memory operation of the loop is
@@ -289,24 +335,52 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int32_t* src = row + min(kb + lane, kv_end - 1);
     __builtin_amdgcn_global_load_lds(PKV_GLB(src), PKV_LDS(id_ring(ring)), 4, 0, 0);
   };
-  auto offsets = [&](int ring, int64_t (&off)[Gm::NI]) {
+  // the logical chunk the tile's swizzle puts at this lane's physical chunk
+  auto chunk_of = [&](int rr) {
+    if constexpr (kFp8)
+      return pch ^ ((rr / Sg::RPL) & (Sg::CPR - 1));
+    else
+      return pch ^ (rr & (Sg::CPR - 1));
+  };
+  auto offsets = [&](int ring, int64_t (&off)[Sg::NI]) {
     const int* ids = id_ring(ring);
 #pragma unroll
-    for (int i = 0; i < Gm::NI; ++i) {
-      const int rr = 16 * wave + Gm::RPI * i + prow;
-      const int lch = pch ^ (rr & (Gm::CPR - 1));
-      off[i] = (int64_t)clamp_index(ids[rr], n_slots) * row_stride + 16 * lch;
+    for (int i = 0; i < Sg::NI; ++i) {
+      const int rr = 16 * wave + Sg::RPI * i + prow;
+      off[i] = (int64_t)clamp_index(ids[rr], n_slots) * row_stride + 16 * chunk_of(rr);
     }
   };
-  auto issue = [&](int stage, const int64_t (&off)[Gm::NI]) {
+  // E4M3 pools: this lane's V chunks of the next block, in registers until
+  // they are widened into the bf16 V tile
+  u32x4 vreg[kFp8 ? Sg::NI : 1];
+  auto issue = [&](int stage, const int64_t (&off)[Sg::NI]) {
     char* st = stage_ptr(stage);
 #pragma unroll
-    for (int i = 0; i < Gm::NI; ++i) {
-      const int rbase = 16 * wave + Gm::RPI * i;
-      __builtin_amdgcn_global_load_lds(PKV_GLB(kbase + off[i]), PKV_LDS(st + rbase * Gm::ROW), 16,
+    for (int i = 0; i < Sg::NI; ++i) {
+      const int rbase = 16 * wave + Sg::RPI * i;
+      __builtin_amdgcn_global_load_lds(PKV_GLB(kbase + off[i]), PKV_LDS(st + rbase * Sg::ROW), 16,
                                        0, 0);
-      __builtin_amdgcn_global_load_lds(PKV_GLB(vbase + off[i]),
-                                       PKV_LDS(st + Gm::TILE + rbase * Gm::ROW), 16, 0, 0);
+      if constexpr (kFp8)
+        vreg[i] = *(const u32x4*)(vbase + off[i]);
+      else
+        __builtin_amdgcn_global_load_lds(PKV_GLB(vbase + off[i]),
+                                         PKV_LDS(st + Sg::KTILE + rbase * Gm::ROW), 16, 0, 0);
+    }
+  };
+  // E4M3 pools: widen this lane's V chunks (row rr, logical code chunk c ->
+  // bf16 chunks 2c, 2c + 1) into the stage's bf16 V tile
+  auto write_v = [&](int stage) {
+    if constexpr (kFp8) {
+      char* vt = stage_ptr(stage) + Sg::KTILE;
+#pragma unroll
+      for (int i = 0; i < Sg::NI; ++i) {
+        const int rr = 16 * wave + Sg::RPI * i + prow;
+        const int c = chunk_of(rr);
+        u32x4 lo, hi;
+        fp8x16_to_bf16x16(vreg[i], lo, hi);
+        *(u32x4*)(vt + swz<D>(rr, 2 * c)) = lo;
+        *(u32x4*)(vt + swz<D>(rr, 2 * c + 1)) = hi;
+      }
     }
   };
 
@@ -323,15 +397,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     tok[n] = t;
     const int tc = min(t, n_new - 1);
     const int64_t qrow = ((int64_t)q0 + tc) * a.n_q_heads + (int64_t)kvh * G + rr % G;
-    const char* qp = (const char*)a.q + qrow * Gm::ROW + 16 * quad;
+    const char* qp = (const char*)a.q + qrow * Gm::ROW;
+    // k-step ks: head_dim 32 ks + 8 quad .. +7 (bf16 K), or the order of the
+    // E4M3 K reads, 64 (ks/2) + 16 quad + 8 (ks%2) .. +7
 #pragma unroll
-    for (int ks = 0; ks < Gm::KSTEPS; ++ks) qf[n][ks] = *(const u32x4*)(qp + 64 * ks);
+    for (int ks = 0; ks < Gm::KSTEPS; ++ks)
+      qf[n][ks] = *(const u32x4*)(qp + (kFp8 ? 128 * (ks / 2) + 32 * quad + 16 * (ks % 2)
+                                             : 64 * ks + 16 * quad));
     limit[n] = a.causal ? min(P + tc, L - 1) : L - 1;
   }
 
   // a negative scale is applied as -scale on -Q (bf16 negation is exact), a
   // zero scale as scale 1 on Q = 0 (every score is exactly 0 either way)
-  float scale2 = a.scale * kLog2e;
+  // E4M3 pools: the K scale joins the softmax scale, the V scale the output
+  float scale2 = a.scale * kLog2e * (kFp8 ? a.kv_scale[0] : 1.f);
+  const float vscale = kFp8 ? a.kv_scale[1] : 1.f;
   if (!(scale2 > 0.f)) {
     const uint32_t flip = scale2 < 0.f ? 0x80008000u : 0u;
     const uint32_t keep = scale2 < 0.f ? 0xFFFFFFFFu : 0u;
@@ -365,8 +445,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // holds, oldest first, S(i+1) D(i) S(i+2), where D(k) = 2*NI tile transfers
     // of block k into stage k % 2 and S(k) = one slot-id transfer for block k
     // into id ring k % 2. Block indices past the end are clamped, so the counts
-    // never change.
-    int64_t off[Gm::NI];
+    // never change. E4M3 pools: D(k) is NI K transfers plus NI V loads into
+    // registers, and block i waits for everything in flight (all of it belongs
+    // to block i) before its V is widened into the tile and S(i+2) is queued.
+    int64_t off[Sg::NI];
     load_ids(0, 0);
     load_ids(1, 1);
     __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
@@ -376,16 +458,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
     // One block: wait for its transfers, queue the next ones, attend.
     auto block = [&](int i, int u, auto masked) {
-      load_ids(i + 2, u);  // ring u held the ids of block i, already consumed
-      __builtin_amdgcn_s_waitcnt(PKV_VMCNT(1));  // S(i+1) and D(i) landed (this wave)
+      if constexpr (kFp8) {
+        __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));  // S(i+1) and D(i) landed (this wave)
+        write_v(u);  // stage u's V tile: block i-2, its last reader, is done
+        load_ids(i + 2, u);
+        __builtin_amdgcn_s_waitcnt(PKV_LGKMCNT0);  // the V writes, before the barrier
+      } else {
+        load_ids(i + 2, u);  // ring u held the ids of block i, already consumed
+        __builtin_amdgcn_s_waitcnt(PKV_VMCNT(1));  // S(i+1) and D(i) landed (this wave)
+      }
       __builtin_amdgcn_s_barrier();              // ... for every wave; block i-1 is done
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       offsets(u ^ 1, off);
       issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
       const char* st = stage_ptr(u);
-      attend_block<D, G, decltype(masked)::value>(st, st + Gm::TILE, qf, o, lacc, m, mseen, bad,
-                                                  first_pass && i == 0, i * kBK, limit, scale2,
-                                                  lane);
+      attend_block<D, G, decltype(masked)::value, KV>(st, st + Sg::KTILE, qf, o, lacc, m, mseen,
+                                                      bad, first_pass && i == 0, i * kBK, limit,
+                                                      scale2, lane);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
     // Blocks that every row sees whole and that end inside the sequence need
@@ -424,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int64_t orow = ((int64_t)q0 + tok[n]) * a.n_q_heads + (int64_t)kvh * G + rr % G;
     const int64_t t_abs = (int64_t)q0 + tok[n];
     if (t_abs < 0 || t_abs >= a.total_q) continue;
-    const float inv = 1.0f / lacc[n][0];  // the row sum over all keys, in every lane of the column
+    const float inv = vscale / lacc[n][0];  // the row sum over all keys, in every lane of the column
     uint16_t* out = (uint16_t*)a.out + orow * D;
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt) {
@@ -439,17 +528,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D>
+template <int D, typename KV>
 hipError_t prefill_for_dim(const PrefillArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   const int bq = kRows / g;
   dim3 grid((a.max_q_len + bq - 1) / bq, a.n_kv_heads, a.batch);
   switch (g) {
-    case 1: prefill_kernel<D, 1><<<grid, kThreads, 0, stream>>>(a); break;
-    case 2: prefill_kernel<D, 2><<<grid, kThreads, 0, stream>>>(a); break;
-    case 4: prefill_kernel<D, 4><<<grid, kThreads, 0, stream>>>(a); break;
-    case 8: prefill_kernel<D, 8><<<grid, kThreads, 0, stream>>>(a); break;
-    case 16: prefill_kernel<D, 16><<<grid, kThreads, 0, stream>>>(a); break;
+    case 1: prefill_kernel<D, 1, KV><<<grid, kThreads, 0, stream>>>(a); break;
+    case 2: prefill_kernel<D, 2, KV><<<grid, kThreads, 0, stream>>>(a); break;
+    case 4: prefill_kernel<D, 4, KV><<<grid, kThreads, 0, stream>>>(a); break;
+    case 8: prefill_kernel<D, 8, KV><<<grid, kThreads, 0, stream>>>(a); break;
+    case 16: prefill_kernel<D, 16, KV><<<grid, kThreads, 0, stream>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -459,7 +548,11 @@ hipError_t prefill_for_dim(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.batch == 0 || a.max_q_len == 0) return hipSuccess;
-  return a.head_dim == 128 ? prefill_for_dim<128>(a, stream) : prefill_for_dim<64>(a, stream);
+  if (a.dtype == PKV_FP8_E4M3)
+    return a.head_dim == 128 ? prefill_for_dim<128, fp8_t>(a, stream)
+                             : prefill_for_dim<64, fp8_t>(a, stream);
+  return a.head_dim == 128 ? prefill_for_dim<128, bf16_t>(a, stream)
+                           : prefill_for_dim<64, bf16_t>(a, stream);
 }
 
 }  // namespace pkv

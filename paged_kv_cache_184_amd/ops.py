@@ -304,11 +304,11 @@ def decode_merge(meta: BatchMeta, n_q_heads: int, head_dim: int, dtype: torch.dt
 
 
 def paged_prefill_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, max_q_len: int,
-                       scale: float, causal: bool = True, out=None, stream=None):
+                       scale: float, causal: bool = True, out=None, stream=None, kv_scales=None):
     """Ragged packed paged prefill (pkv_paged_prefill_attn). q: [T_q, Hq, D]."""
-    pool = make_pool(k_pool, v_pool)
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _need(q.is_contiguous() and q.dim() == 3 and q.shape[2] == pool.head_dim, "q shape")
-    _need(dtype_code(q.dtype) == pool.dtype, "q dtype must match the pools")
+    _need(q.dtype == io_dtype(k_pool.dtype), "q dtype must match the pools (bf16 for E4M3 pools)")
     if out is None:
         out = torch.empty_like(q)
     _need(out.is_contiguous() and out.shape == q.shape and out.dtype == q.dtype, "out")
@@ -399,8 +399,8 @@ def prepare_metadata(meta: BatchMeta, mode, split, kv_indptr_out=None, loc_out=N
 
 
 def prepare_prefill(q, k_pool, v_pool, layer, meta: BatchMeta, max_q_len, scale, causal, out,
-                    stream=None):
-    pool = make_pool(k_pool, v_pool)
+                    stream=None, kv_scales=None):
+    pool = make_pool(k_pool, v_pool, kv_scales)
     return PreparedCall("pkv_paged_prefill_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
                         C.byref(meta), q.shape[0], max_q_len, scale, 1 if causal else 0,
                         out.data_ptr(), None, keep=(pool, meta), stream=stream)

@@ -8,6 +8,8 @@ Covered:
 - decode parity for g = 1, 2, 4, 8, 16 and head_dim 64 / 128, with several
   splits, ragged lengths and NaN codes in every slot no request maps;
 - the fused step (store, then attend), with its stored codes bit-exact;
+- packed prefill over FP8 pools, after the quantising store of the new
+  tokens, causal and not, for several group sizes and both head_dims;
 - run-to-run determinism;
 - the B=1, 32K-context workload.
 """
@@ -147,3 +149,34 @@ def test_b1_32k_fp8():
     ref = O.decode_attention_fp8(q.float().cpu().numpy(), kh, vh, scales, 0, r2t,
                                  np.zeros(1, np.int32), np.array([32768], np.int32), b.scale)
     compare(out.float().cpu().numpy(), ref, "bf16", "fp8 B=1 32K")
+
+
+@pytest.mark.parametrize("hq,hkv,d,causal", [(32, 8, 128, True), (32, 8, 128, False),
+                                             (16, 4, 64, True), (8, 8, 128, True),
+                                             (64, 4, 128, True), (32, 2, 64, False)])
+def test_prefill_fp8_parity(hq, hkv, d, causal):
+    lens = np.array([300, 70, 1, 129, 700, 64, 5])
+    n_new = np.array([64, 70, 1, 33, 200, 0, 5])
+    scales = np.float32([[0.02, 0.015]])
+    b = W.custom(f"fp8_prefill_{hq}_{d}", n_layers=1, n_slots=4096, n_q_heads=hq, n_kv_heads=hkv,
+                 head_dim=d, dtype="bf16", seq_lens=lens, n_new=n_new, seed=640 + hq + d)
+    vals = W.host_values(b, 641 + d, poison_unreferenced=True)
+    kc = O.quantize(vals.k_pool, scales[0, 0])
+    vc = O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens),
+                         to_dev(b.qo_indptr))
+    loc = torch.empty(b.total_q, dtype=torch.int32, device=DEV)
+    ops.build_metadata(meta, ops.PKV_MODE_PREFILL, None, None, loc, None)
+    ops.kv_store(kd, vd, 0, to_dev(vals.k_new, torch.bfloat16), to_dev(vals.v_new, torch.bfloat16),
+                 loc, kv_scales=sd)
+    q = to_dev(vals.q, torch.bfloat16)
+    out = ops.paged_prefill_attn(q, kd, vd, 0, meta, b.max_q_len, b.scale, causal, kv_scales=sd)
+    torch.cuda.synchronize()
+    loc_h = O.prefill_locations(b.req_to_token, b.req_pool_indices, b.seq_lens, b.qo_indptr)
+    kc2, vc2 = O.kv_store_fp8(kc, vc, 0, vals.k_new, vals.v_new, loc_h, scales)
+    assert np.array_equal(kd.cpu().numpy(), kc2) and np.array_equal(vd.cpu().numpy(), vc2)
+    ref = O.prefill_attention_fp8(vals.q, kc2, vc2, scales, 0, b.req_to_token,
+                                  b.req_pool_indices, b.seq_lens, b.qo_indptr, b.scale,
+                                  causal=causal)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill g={hq // hkv} d={d} causal={causal}")
