@@ -28,7 +28,7 @@
  *   Query head h of a request reads KV head h / (n_q_heads / n_kv_heads).
  *
  * Supported: dtype F32 or BF16 (Q, K, V and output share it; accumulation is
- * always fp32; prefill is BF16 only), head_dim 64 or 128, group size
+ * always fp32; prefill takes BF16 or FP8_E4M3 pools), head_dim 64 or 128, group size
  * n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}. FP8_E4M3 pools (one-byte codes
  * with per-layer K and V scales, see pkv_kv_pool) hold K/V for the decode
  * and prefill entry points and pkv_kv_store; there q, the new K/V rows and the
