@@ -286,8 +286,9 @@ typedef struct pkv_prefix_groups {
 
 /* Split plan: the prefix of a request forms splits under a cap of
  * max_splits / 2 (partial indices first), its private suffix of L_b - P_b keys
- * splits under the rest of the cap (after them); max_splits >= 2; BF16 pools
- * only. The workspace is sized as for pkv_paged_decode_attn. */
+ * splits under the rest of the cap (after them); max_splits >= 2; BF16 or
+ * FP8_E4M3 pools (F32: PKV_EUNSUPPORTED). The workspace is sized as for
+ * pkv_paged_decode_attn. */
 pkv_status pkv_cascade_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                    int32_t n_q_heads, const pkv_batch_meta* meta,
                                    const pkv_prefix_groups* groups, float scale,

@@ -370,8 +370,8 @@ pkv_status pkv_cascade_decode_attn(const pkv_kv_pool* pool, int32_t layer, const
   pkv_status s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, workspace, ws_bytes, &a);
   if (s != PKV_OK) return s;
   if (!groups) return fail(PKV_EINVAL, "groups is NULL");
-  if (pool->dtype != PKV_BF16)
-    return fail(PKV_EUNSUPPORTED, "cascade decode supports BF16 only (MFMA prefix kernel)");
+  if (pool->dtype != PKV_BF16 && pool->dtype != PKV_FP8_E4M3)
+    return fail(PKV_EUNSUPPORTED, "cascade decode supports BF16 and FP8_E4M3 pools (MFMA prefix)");
   if (split.max_splits < 2) return fail(PKV_EINVAL, "cascade decode needs max_splits >= 2");
   if (groups->n_groups < 0 || groups->n_groups > kMaxBatch)
     return fail(PKV_EINVAL, "n_groups %d outside [0, %d]", groups->n_groups, kMaxBatch);

@@ -20,8 +20,9 @@
 //     operand, V staged through a per-wave LDS tile and read back
 //     transposed), so each K/V fragment serves all of the tile's members.
 //   * z >= n_groups * n_tiles: the regular decode work of request
-//     z - n_groups * n_tiles (VALU kernel for g <= 4, MFMA kernel for g >= 8),
-//     whose split plan places its suffix splits after the prefix ones.
+//     z - n_groups * n_tiles (bf16 pools: VALU kernel for g <= 4, MFMA kernel
+//     for g >= 8; E4M3 pools: MFMA kernel), whose split plan places its suffix
+//     splits after the prefix ones.
 // Both kinds share one LDS layout (the MFMA V tiles also hold the wave-merge
 // rows), so the launch keeps two workgroups per CU.
 #include "decode_mfma.hpp"
@@ -43,12 +44,14 @@ static_assert(decode_impl::kSuper == kSB * kBlk, "the two decode loops stage equ
 // the group, cpm = 16 / g. Column c is (member tile * cpm + c / g, head c % g).
 // The prefix's split plan and slots are those of the group's first member; a
 // member whose own prefix length differs gets no prefix partials here.
-template <int D>
+template <int D, typename KV>
 __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s, int grp,
                                              int tile, char (*vs0)[MGeo<D>::VST],
                                              int (*slot_lds)[kSB * kBlk],
                                              float (*red_ml)[kCols][2]) {
   using Gm = MGeo<D>;
+  constexpr bool kFp8 = sizeof(KV) == 1;
+  constexpr int ROW = KVLd<D, KV>::ROW;  // bytes of a stored (slot, KV head) row
   static_assert(kCols * D * 4 <= Gm::VST, "a wave's merge rows fit in its V tile");
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -78,7 +81,7 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s
   const int32_t* row =
       a.req_to_token + (int64_t)clamp_index(a.req_pool_indices[b0], a.n_rows) * a.stride;
   const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
-  const int64_t row_stride = (int64_t)a.n_kv_heads * Gm::ROW;
+  const int64_t row_stride = (int64_t)a.n_kv_heads * ROW;
 
   // this lane's column: member bj, head hh; zero query unless it is a member
   // of this tile with the group's prefix length
@@ -86,19 +89,25 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s
   const int bj = clamp_index(a.group_members[m0 + j0 + min(col / gq, nm - 1)], a.batch);
   const bool valid = col < nm * gq && plan_for(a, bj).P == pl.P;
   u32x4 qf[1][Gm::KS];
-  const char* qp = (const char*)a.q +
-                   ((int64_t)bj * a.n_q_heads + (int64_t)kvh * gq + hh) * Gm::ROW + 16 * quad;
+  const char* qp =
+      (const char*)a.q + ((int64_t)bj * a.n_q_heads + (int64_t)kvh * gq + hh) * Gm::ROW;
+  // k-step order of the K loads (E4M3 loads carry two k-steps), as in the
+  // MFMA decode kernel
 #pragma unroll
   for (int ks = 0; ks < Gm::KS; ++ks) {
-    const u32x4 v = *(const u32x4*)(qp + 64 * ks);
+    const int byte = kFp8 ? 128 * (ks / 2) + 32 * quad + 16 * (ks % 2) : 64 * ks + 16 * quad;
+    const u32x4 v = *(const u32x4*)(qp + byte);
     qf[0][ks] = valid ? v : u32x4{0u, 0u, 0u, 0u};
   }
-  const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW;
-  const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW;
+  const char* kbase = (const char*)a.k + (int64_t)kvh * ROW;
+  const char* vbase = (const char*)a.v + (int64_t)kvh * ROW;
+  // E4M3 pools: the K scale joins the softmax scale, the V scale the outputs
+  const float kscale = kFp8 ? a.kv_scale[0] : 1.f;
+  const float vscale = kFp8 ? a.kv_scale[1] : 1.f;
   WaveState<D, 1> st;
   init_state(st);
-  wave_loop<D, 1>(st, slot_lds[wave], vs0[wave], row, n_slots, wlo, whi, qf, kbase, vbase,
-                  row_stride, a.scale * kLog2e, lane);
+  wave_loop<D, 1, KV>(st, slot_lds[wave], vs0[wave], row, n_slots, wlo, whi, qf, kbase, vbase,
+                      row_stride, a.scale * kLog2e * kscale, lane);
 
   // Hand the wave's (m, l, O) per column to LDS (O rows into the wave's own V
   // tile, whose transpose reads have returned); wave 0 also records each
@@ -107,7 +116,7 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s
 #pragma unroll
   for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[0][dt][r];
+    for (int r = 0; r < 4; ++r) mine[col * D + 16 * dt + 4 * quad + r] = st.o[0][dt][r] * vscale;
   if (quad == 0) {
     red_ml[wave][col][0] = st.m[0];
     red_ml[wave][col][1] = st.lsum[0][0];
@@ -138,7 +147,7 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s
   }
 }
 
-template <int D, int G>
+template <int D, int G, typename KV>
 __global__ __launch_bounds__(64 * kW, 2) void cascade_kernel(DecodeArgs a, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) char vs0[kW][MGeo<D>::VST];
   __shared__ int slot_lds[kW][kSB * kBlk];
@@ -149,12 +158,12 @@ __global__ __launch_bounds__(64 * kW, 2) void cascade_kernel(DecodeArgs a, int n
   const int n_pz = a.n_groups * n_tiles;
   if (z < n_pz) {
     if (s < prefix_cap(a.split.max_splits))
-      prefix_split<D>(a, kvh, s, z / n_tiles, z % n_tiles, vs0, slot_lds, red_ml);
+      prefix_split<D, KV>(a, kvh, s, z / n_tiles, z % n_tiles, vs0, slot_lds, red_ml);
     return;
   }
   float(*ml)[G][2] = (float(*)[G][2]) & red_ml[0][0][0];
-  if constexpr (G >= 8) {
-    mfma_split<D, G>(a, kvh, s, z - n_pz, vs0, slot_lds, ml);
+  if constexpr (G >= 8 || sizeof(KV) == 1) {
+    mfma_split<D, G, KV>(a, kvh, s, z - n_pz, vs0, slot_lds, ml);
   } else {
     static_assert(G * D * 4 <= MGeo<D>::VST, "a wave's merge rows fit in its V tile");
     decode_impl::decode_split<bf16_t, D, G>(a, kvh, s, z - n_pz, slot_lds, (float*)&vs0[0][0],
@@ -162,16 +171,16 @@ __global__ __launch_bounds__(64 * kW, 2) void cascade_kernel(DecodeArgs a, int n
   }
 }
 
-template <int D>
+template <int D, typename KV>
 hipError_t cascade_for_dim(const DecodeArgs& a, int n_tiles, hipStream_t stream) {
   const int gq = a.n_q_heads / a.n_kv_heads;
   dim3 grid(a.n_kv_heads, a.split.max_splits, a.n_groups * n_tiles + a.batch);
   switch (gq) {
-    case 1: cascade_kernel<D, 1><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
-    case 2: cascade_kernel<D, 2><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
-    case 4: cascade_kernel<D, 4><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
-    case 8: cascade_kernel<D, 8><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
-    case 16: cascade_kernel<D, 16><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
+    case 1: cascade_kernel<D, 1, KV><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
+    case 2: cascade_kernel<D, 2, KV><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
+    case 4: cascade_kernel<D, 4, KV><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
+    case 8: cascade_kernel<D, 8, KV><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
+    case 16: cascade_kernel<D, 16, KV><<<grid, 64 * kW, 0, stream>>>(a, n_tiles); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -187,8 +196,11 @@ int cascade_tiles(int n_q_heads, int n_kv_heads, int max_members) {
 hipError_t launch_cascade_partials(const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   const int n_tiles = a.n_groups > 0 ? cascade_tiles(a.n_q_heads, a.n_kv_heads, a.max_members) : 0;
-  return a.head_dim == 128 ? cascade_for_dim<128>(a, n_tiles, stream)
-                           : cascade_for_dim<64>(a, n_tiles, stream);
+  if (a.dtype == PKV_FP8_E4M3)
+    return a.head_dim == 128 ? cascade_for_dim<128, fp8_t>(a, n_tiles, stream)
+                             : cascade_for_dim<64, fp8_t>(a, n_tiles, stream);
+  return a.head_dim == 128 ? cascade_for_dim<128, bf16_t>(a, n_tiles, stream)
+                           : cascade_for_dim<64, bf16_t>(a, n_tiles, stream);
 }
 
 }  // namespace pkv

@@ -245,9 +245,9 @@ def make_prefix_groups(prefix_len: torch.Tensor, group_indptr: torch.Tensor,
 
 def cascade_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta,
                         groups: _lib.PrefixGroups, scale: float, split: SplitCfg,
-                        workspace: torch.Tensor, out=None, stream=None):
+                        workspace: torch.Tensor, out=None, stream=None, kv_scales=None):
     """Decode with each group's shared prefix read once (pkv_cascade_decode_attn)."""
-    pool = make_pool(k_pool, v_pool)
+    pool = make_pool(k_pool, v_pool, kv_scales)
     _q_check(q, pool, meta.batch)
     if out is None:
         out = torch.empty_like(q)
@@ -376,8 +376,8 @@ def prepare_decode_step(q, k_pool, v_pool, layer, meta: BatchMeta, scale, split,
 
 
 def prepare_cascade_decode(q, k_pool, v_pool, layer, meta: BatchMeta, groups, scale, split,
-                           workspace, out, stream=None):
-    pool = make_pool(k_pool, v_pool)
+                           workspace, out, stream=None, kv_scales=None):
+    pool = make_pool(k_pool, v_pool, kv_scales)
     return PreparedCall("pkv_cascade_decode_attn", C.byref(pool), layer, q.data_ptr(), q.shape[1],
                         C.byref(meta), C.byref(groups), scale, split, workspace.data_ptr(),
                         workspace.numel(), out.data_ptr(), None, keep=(pool, meta, groups),

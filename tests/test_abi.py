@@ -161,8 +161,8 @@ def test_rope_kv_store_rejects(lib):
 
 
 def test_fp8_pool_rules(lib):
-    """E4M3 pools need 8-byte aligned kv_scales; rope_kv_store and cascade
-    decode reject them; the merge's dtype is the output's (F32/BF16).
+    """E4M3 pools need 8-byte aligned kv_scales; rope_kv_store rejects them;
+    cascade decode rejects F32 pools; the merge's dtype is the output's (F32/BF16).
     Only error paths are called: nothing is launched."""
     fp8 = _lib.PKV_FP8_E4M3
     store = lib.pkv_kv_store
@@ -179,8 +179,11 @@ def test_fp8_pool_rules(lib):
     assert lib.pkv_paged_prefill_attn(C.byref(_pool(dtype=fp8)), 0, 16, 4, C.byref(meta_qo), 1, 1,
                                       0.125, 1, 16, None) == _lib.PKV_EINVAL  # no scales
     groups = _lib.PrefixGroups(16, 32, 48, 1, 2, 2, 0)
-    assert lib.pkv_cascade_decode_attn(C.byref(ok_pool), 0, 16, 4, C.byref(meta), C.byref(groups),
-                                       0.125, _split(), 256, 1 << 20, 16,
+    assert lib.pkv_cascade_decode_attn(C.byref(_pool(dtype=fp8)), 0, 16, 4, C.byref(meta),
+                                       C.byref(groups), 0.125, _split(), 256, 1 << 20, 16,
+                                       None) == _lib.PKV_EINVAL  # no scales
+    assert lib.pkv_cascade_decode_attn(C.byref(_pool(dtype=_lib.PKV_F32)), 0, 16, 4, C.byref(meta),
+                                       C.byref(groups), 0.125, _split(), 256, 1 << 20, 16,
                                        None) == _lib.PKV_EUNSUPPORTED
     assert lib.pkv_decode_merge(C.byref(meta), 4, 64, fp8, _split(), 256, 1 << 20, 16,
                                 None) == _lib.PKV_EDTYPE

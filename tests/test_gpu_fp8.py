@@ -10,6 +10,7 @@ Covered:
 - the fused step (store, then attend), with its stored codes bit-exact;
 - packed prefill over FP8 pools, after the quantising store of the new
   tokens, causal and not, for several group sizes and both head_dims;
+- cascade (shared-prefix) decode over FP8 pools;
 - run-to-run determinism;
 - the B=1, 32K-context workload.
 """
@@ -180,3 +181,26 @@ def test_prefill_fp8_parity(hq, hkv, d, causal):
                                   b.req_pool_indices, b.seq_lens, b.qo_indptr, b.scale,
                                   causal=causal)
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill g={hq // hkv} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
+def test_cascade_fp8_parity(hq, hkv, d):
+    from tests.test_gpu_cascade import groups_for, shared_batch
+    lens = [1100, 1025, 1024, 40, 300, 300, 777, 2000]
+    groups = [[0, 1, 2], [3], [4, 5]]
+    P = [1024, 33, 0]
+    scales = np.float32([[0.02, 0.01]])
+    b = shared_batch(f"fp8_cascade{hq}", lens, groups, P, 650, hq, hkv, d)
+    vals = W.host_values(b, 651)
+    kc, vc = O.quantize(vals.k_pool, scales[0, 0]), O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    q = to_dev(vals.q, torch.bfloat16)
+    split = ops.split_cfg(8, 0, 256)
+    ws = ops.alloc_decode_workspace(b.batch, hq, d, split.max_splits)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens))
+    out = ops.cascade_decode_attn(q, kd, vd, 0, meta, groups_for(b, groups, P), b.scale, split, ws,
+                                  kv_scales=sd)
+    torch.cuda.synchronize()
+    ref = O.decode_attention_fp8(vals.q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
+                                 b.seq_lens, b.scale)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 cascade g={hq // hkv} d={d}")
