@@ -43,4 +43,6 @@ from .fp8_kv import (  # noqa: F401
     kv_store_fp8,
     decode_attention_fp8,
     prefill_attention_fp8,
+    rope_fp32,
+    rope_kv_store_fp8,
 )

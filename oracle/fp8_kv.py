@@ -19,13 +19,17 @@ below are readings, each listed in the design notes:
       magnitudes beyond 448 saturated to 448; NaN gives a NaN code.
   R20 attention over an FP8 pool is the attention over the values the codes
       stand for: the decode definition applied to the dequantised pools.
+  R21 the fused RoPE store into an FP8 pool decides each k code on the fp32
+      rotation with every product and sum rounded once, in the order
+      a' = fl(fl(a c) - fl(b s)), b' = fl(fl(b c) + fl(a s)); v is quantised
+      unrotated; q is rotated as for the other pools.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .paged_attention import decode_attention, prefill_attention
+from .paged_attention import apply_rope, decode_attention, prefill_attention, rope_pairs
 
 E4M3_MAX = 448.0  # R17: 0x7E = 2^8 * (1 + 6/8)
 
@@ -107,3 +111,33 @@ def prefill_attention_fp8(q, k_codes, v_codes, kv_scales, layer, req_to_token, r
     vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)
     return prefill_attention(q, kp, vp, 0, req_to_token, req_pool_indices, seq_lens, qo_indptr,
                              scale, causal=causal)
+
+
+def rope_fp32(x, positions, freqs_cis, interleaved=True):
+    """The rotation of R21 in fp32: each product and each sum rounded once to
+    fp32 (numpy float32 arithmetic), returned as float32 [T, H, D]."""
+    x = np.asarray(x, np.float32)
+    T, H, D = x.shape
+    tab = np.asarray(freqs_cis, np.float32)
+    out = x.copy()
+    for t in range(T):
+        p = int(positions[t])
+        for i, (a, b) in enumerate(rope_pairs(D, interleaved)):
+            c, s = tab[p, i, 0], tab[p, i, 1]
+            ac, bs = x[t, :, a] * c, x[t, :, b] * s
+            bc, as_ = x[t, :, b] * c, x[t, :, a] * s
+            out[t, :, a] = ac - bs
+            out[t, :, b] = bc + as_
+    return out
+
+
+def rope_kv_store_fp8(q, k_new, v_new, positions, freqs_cis, k_codes, v_codes, layer, loc,
+                      kv_scales, interleaved=True):
+    """RoPE on the new tokens' q and k, then the quantising store of (rotated
+    k, v) into the code pools (R15, R19, R21): returns (q_rot fp64, k_codes',
+    v_codes')."""
+    q_rot = apply_rope(q, positions, freqs_cis, interleaved)
+    k_rot = rope_fp32(k_new, positions, freqs_cis, interleaved)
+    kc, vc = kv_store_fp8(k_codes, v_codes, layer, k_rot, np.asarray(v_new, np.float32), loc,
+                          kv_scales)
+    return q_rot, kc, vc

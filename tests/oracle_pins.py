@@ -621,6 +621,70 @@ def pin_prefill_fp8_library(O, seed=34):
         np.testing.assert_allclose(out[lo:hi], ref, rtol=0, atol=1e-12)
 
 
+def pin_rope_fp32_closed_forms(O, seed=35):
+    """The fp32 rotation: a table of (1, 0) is the identity and one of (0, 1)
+    the exact quarter turn (a, b) -> (-b, a); for general angles the result is
+    within 2^-22 (|a c| + |b s|) of the fp64 rotation (two roundings of the
+    products, one of the sum)."""
+    rng = np.random.default_rng(seed)
+    T, H, D = 3, 2, 8
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    pos = np.array([0, 1, 2])
+    tab = np.zeros((3, D // 2, 2), np.float32)
+    tab[0, :, 0] = 1.0
+    tab[1, :, 1] = 1.0
+    ang = rng.uniform(0, 6.3, D // 2)
+    tab[2, :, 0], tab[2, :, 1] = np.cos(ang), np.sin(ang)
+    for inter in (True, False):
+        out = O.rope_fp32(x, pos, tab, inter)
+        assert out.dtype == np.float32
+        assert np.array_equal(out[0], x[0])
+        pairs = [(2 * i, 2 * i + 1) for i in range(D // 2)] if inter else \
+            [(i, i + D // 2) for i in range(D // 2)]
+        for a, b in pairs:
+            assert np.array_equal(out[1, :, a], -x[1, :, b])
+            assert np.array_equal(out[1, :, b], x[1, :, a])
+        x64 = x.astype(np.float64)
+        for i, (a, b) in enumerate(pairs):
+            c, s = float(tab[2, i, 0]), float(tab[2, i, 1])
+            ref_a = x64[2, :, a] * c - x64[2, :, b] * s
+            ref_b = x64[2, :, b] * c + x64[2, :, a] * s
+            bound_a = 2.0 ** -22 * (np.abs(x64[2, :, a] * c) + np.abs(x64[2, :, b] * s))
+            bound_b = 2.0 ** -22 * (np.abs(x64[2, :, b] * c) + np.abs(x64[2, :, a] * s))
+            assert np.all(np.abs(out[2, :, a] - ref_a) <= bound_a)
+            assert np.all(np.abs(out[2, :, b] - ref_b) <= bound_b)
+
+
+def pin_rope_kv_store_fp8(O, seed=36):
+    """Fused RoPE store into code pools: with an identity table it is the
+    quantising store of (k, v); with a quarter turn the k codes are those of
+    (-b, a); q is the fp64 rotation; unaddressed bytes stay."""
+    rng = np.random.default_rng(seed)
+    T, Hq, Hkv, D, S = 4, 4, 2, 8, 16
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    kp = rng.integers(0, 0x7E, (2, S, Hkv, D)).astype(np.uint8)
+    vp = rng.integers(0, 0x7E, (2, S, Hkv, D)).astype(np.uint8)
+    scales = np.float32([[0.5, 0.25], [0.02, 0.03]])
+    loc = np.array([3, -1, 9, 0])
+    tab = np.zeros((2, D // 2, 2), np.float32)
+    tab[0, :, 0] = 1.0
+    tab[1, :, 1] = 1.0
+    qr, kc, vc = O.rope_kv_store_fp8(q, k, v, np.zeros(T, int), tab, kp, vp, 1, loc, scales)
+    kc2, vc2 = O.kv_store_fp8(kp, vp, 1, k, v, loc, scales)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+    assert np.allclose(qr, q, atol=0)
+    qr, kc, vc = O.rope_kv_store_fp8(q, k, v, np.ones(T, int), tab, kp, vp, 1, loc, scales)
+    turned = np.empty_like(k)
+    turned[:, :, 0::2], turned[:, :, 1::2] = -k[:, :, 1::2], k[:, :, 0::2]
+    kc3, _ = O.kv_store_fp8(kp, vp, 1, turned, v, loc, scales)
+    assert np.array_equal(kc, kc3) and np.array_equal(vc, vc2)
+    qt = np.empty_like(q)
+    qt[:, :, 0::2], qt[:, :, 1::2] = -q[:, :, 1::2], q[:, :, 0::2]
+    assert np.allclose(qr, qt, atol=0)
+
+
 ALL_PINS = [
     pin_decode_vs_sdpa, pin_prefill_vs_sdpa, pin_golden_two_keys, pin_golden_prefill,
     pin_closed_forms, pin_gqa_mapping, pin_slot_permutation, pin_split_merge,
@@ -630,5 +694,6 @@ ALL_PINS = [
     pin_rope_complex, pin_rope_half_split_is_permuted_interleaved, pin_rope_standard_table,
     pin_rope_kv_store, pin_e4m3_decode_library, pin_e4m3_spec_values, pin_e4m3_encode_library,
     pin_e4m3_saturation_and_nan, pin_quantize_fp32_quotient, pin_kv_store_fp8,
-    pin_decode_fp8_library, pin_prefill_fp8_library,
+    pin_decode_fp8_library, pin_prefill_fp8_library, pin_rope_fp32_closed_forms,
+    pin_rope_kv_store_fp8,
 ]

@@ -81,6 +81,10 @@ FP8_MUTATIONS = {
     "prefill_fp8_ignores_v_scale": ("vp = dequantize(np.asarray(v_codes)[layer:layer + 1], vs)\n    return prefill_attention",
                                     "vp = dequantize(np.asarray(v_codes)[layer:layer + 1], 1.0)\n    return prefill_attention"),
     "prefill_fp8_not_causal": ("scale, causal=causal)", "scale, causal=False)"),
+    "rope_fp32_sin_sign": ("out[t, :, a] = ac - bs", "out[t, :, a] = ac + bs"),
+    "rope_fp32_reads_rotated": ("out[t, :, b] = bc + as_", "out[t, :, b] = bc + out[t, :, a] * s"),
+    "rope_fp8_store_unrotated": ("kc, vc = kv_store_fp8(k_codes, v_codes, layer, k_rot,",
+                                 "kc, vc = kv_store_fp8(k_codes, v_codes, layer, k_new,"),
     "decode_fp8_layer0": ("kp = dequantize(np.asarray(k_codes)[layer:layer + 1], ks)",
                           "kp = dequantize(np.asarray(k_codes)[0:1], ks)"),
 }
