@@ -175,8 +175,11 @@ pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_ne
  * aligned; q_out may equal q (in place); both NULL to rotate only k.
  * k_new, v_new: device [n_tokens, n_kv_heads, head_dim], 16-byte aligned, not
  * modified. positions, loc: device int32 [n_tokens]. freqs_cis: device float
- * [max_pos, head_dim/2, 2], 8-byte aligned. F32 and BF16 pools (FP8_E4M3:
- * PKV_EUNSUPPORTED). */
+ * [max_pos, head_dim/2, 2], 8-byte aligned. FP8_E4M3 pools: q, q_out,
+ * k_new and v_new are BF16; k is rotated in fp32 with each product and sum
+ * rounded once (a' = fl(fl(a cos) - fl(b sin)), b' = fl(fl(b cos) +
+ * fl(a sin)), no fused multiply-add) and its codes are decided on that value
+ * as pkv_kv_store decides them; v is quantised unrotated. */
 pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* q, void* q_out,
                              int32_t n_q_heads, const void* k_new, const void* v_new,
                              const int32_t* positions, const float* freqs_cis, int32_t max_pos,

@@ -238,8 +238,6 @@ pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void*
   if ((s = check_pool(pool, layer)) != PKV_OK) return s;
   if (n_tokens < 0) return fail(PKV_EINVAL, "n_tokens must be >= 0");
   if (n_tokens > (int64_t)1 << 40) return fail(PKV_EINVAL, "n_tokens too large");
-  if (pool->dtype == PKV_FP8_E4M3)
-    return fail(PKV_EUNSUPPORTED, "rope_kv_store supports F32 and BF16 pools");
   if (interleaved != 0 && interleaved != 1) return fail(PKV_EINVAL, "interleaved must be 0 or 1");
   if (max_pos <= 0) return fail(PKV_EINVAL, "max_pos must be > 0");
   if ((q == nullptr) != (q_out == nullptr))
@@ -251,7 +249,8 @@ pkv_status pkv_rope_kv_store(const pkv_kv_pool* pool, int32_t layer, const void*
   if (!aligned16(k_new) || !aligned16(v_new) || (q && (!aligned16(q) || !aligned16(q_out))))
     return fail(PKV_EALIGN, "q / q_out / k_new / v_new must be 16-byte aligned");
   if (((uintptr_t)freqs_cis & 7) != 0) return fail(PKV_EALIGN, "freqs_cis must be 8-byte aligned");
-  pkv::RopeArgs r;
+  pkv::RopeArgs r{};
+  r.kv_scale = pool->dtype == PKV_FP8_E4M3 ? pool->kv_scales + 2 * (int64_t)layer : nullptr;
   r.k_layer = a_k_layer(pool, layer);
   r.v_layer = a_v_layer(pool, layer);
   r.n_slots = pool->n_slots;

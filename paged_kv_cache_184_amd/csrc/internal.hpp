@@ -114,6 +114,7 @@ struct RopeArgs {
   int32_t interleaved;
   const int32_t* loc;  // [T]
   int64_t n_tokens;
+  const float* kv_scale;  // E4M3 pools: this layer's (k_scale, v_scale)
 };
 
 hipError_t launch_rope_kv_store(const RopeArgs& r, hipStream_t stream);

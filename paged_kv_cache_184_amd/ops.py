@@ -145,12 +145,15 @@ def kv_store(k_pool, v_pool, layer: int, k_new, v_new, loc, stream=None, kv_scal
 
 
 def rope_kv_store(k_pool, v_pool, layer: int, k_new, v_new, positions, freqs_cis, loc,
-                  q=None, q_out=None, interleaved: bool = True, stream=None) -> None:
+                  q=None, q_out=None, interleaved: bool = True, stream=None,
+                  kv_scales=None) -> None:
     """Rotary embedding of the new tokens fused with their store
     (pkv_rope_kv_store): pool[layer, loc[t]] = (rope(k_new[t]), v_new[t]) and,
-    when q is given, q_out = rope(q) (q_out defaults to q: in place)."""
-    pool = make_pool(k_pool, v_pool)
-    _need(k_new.dtype == k_pool.dtype and v_new.dtype == k_pool.dtype, "dtype mismatch")
+    when q is given, q_out = rope(q) (q_out defaults to q: in place). E4M3
+    pools take bf16 rows and store codes under the layer's scales."""
+    pool = make_pool(k_pool, v_pool, kv_scales)
+    io = io_dtype(k_pool.dtype)
+    _need(k_new.dtype == io and v_new.dtype == io, "dtype mismatch")
     _need(k_new.is_contiguous() and v_new.is_contiguous(), "k_new / v_new must be contiguous")
     _need(loc.dtype == torch.int32 and loc.is_contiguous(), "loc must be contiguous int32")
     _need(positions.dtype == torch.int32 and positions.is_contiguous(),
@@ -165,7 +168,7 @@ def rope_kv_store(k_pool, v_pool, layer: int, k_new, v_new, positions, freqs_cis
     hq = 0
     if q is not None:
         q_out = q if q_out is None else q_out
-        _need(q.dtype == k_pool.dtype and q.is_contiguous() and q_out.is_contiguous(), "q layout")
+        _need(q.dtype == io and q.is_contiguous() and q_out.is_contiguous(), "q layout")
         _need(q.shape[0] == n and q_out.shape == q.shape, "q shape")
         hq = q.shape[1]
     _check(lib().pkv_rope_kv_store(C.byref(pool), layer, _ptr(q), _ptr(q_out), hq,

@@ -161,7 +161,7 @@ def test_rope_kv_store_rejects(lib):
 
 
 def test_fp8_pool_rules(lib):
-    """E4M3 pools need 8-byte aligned kv_scales; rope_kv_store rejects them;
+    """E4M3 pools need 8-byte aligned kv_scales (every entry point checks);
     cascade decode rejects F32 pools; the merge's dtype is the output's (F32/BF16).
     Only error paths are called: nothing is launched."""
     fp8 = _lib.PKV_FP8_E4M3
@@ -172,8 +172,8 @@ def test_fp8_pool_rules(lib):
     ok_pool = _pool(dtype=fp8, kv_scales=64)
     assert store(C.byref(ok_pool), 0, 24, 16, 16, 1, None) == _lib.PKV_EALIGN
     assert store(C.byref(ok_pool), 0, 16, 16, 16, 0, None) == _lib.PKV_OK  # no-op
-    assert lib.pkv_rope_kv_store(C.byref(ok_pool), 0, None, None, 0, 16, 16, 16, 8, 4, 1, 16, 1,
-                                 None) == _lib.PKV_EUNSUPPORTED
+    assert lib.pkv_rope_kv_store(C.byref(_pool(dtype=fp8)), 0, None, None, 0, 16, 16, 16, 8, 4, 1,
+                                 16, 1, None) == _lib.PKV_EINVAL  # no scales
     meta = _meta()
     meta_qo = _meta(qo_indptr=64)
     assert lib.pkv_paged_prefill_attn(C.byref(_pool(dtype=fp8)), 0, 16, 4, C.byref(meta_qo), 1, 1,

@@ -11,8 +11,17 @@ Covered:
 - packed prefill over FP8 pools, after the quantising store of the new
   tokens, causal and not, for several group sizes and both head_dims;
 - cascade (shared-prefix) decode over FP8 pools;
+- the fused RoPE store: k codes (decided on the fp32 rotation) and v codes
+  bit-exact, q within the rounding bound, untouched bytes and skipped
+  locations, both pairings and head_dims;
 - run-to-run determinism;
 - the B=1, 32K-context workload.
+
+V scales are powers of two: then every value a V code stands for is a bf16
+value, and an output that equals one of them (a row that sees one key) is
+exact, as with bf16 pools. With other V scales such an output could carry up
+to half a bf16 ulp, which exceeds the 1e-2 bound for magnitudes of 4 and
+more. K scales are arbitrary (they only scale the scores).
 """
 
 import numpy as np
@@ -86,7 +95,7 @@ def test_kv_store_fp8_codes_bit_exact(d):
                                       (64, 4, 128), (32, 2, 64)])
 def test_decode_fp8_parity(hq, hkv, d):
     lens = [1, 15, 16, 17, 100, 511, 1500, 2049, 0]
-    scales = [[0.02, 0.01], [4.0 / 448, 3.0 / 448]]
+    scales = [[0.02, 2.0 ** -6], [4.0 / 448, 2.0 ** -7]]
     b, vals, kc, vc = fp8_batch(610 + hq + d, hq, hkv, d, lens, scales)
     q = np.zeros((b.batch, hq, d), np.float32)
     q[np.asarray(lens) > 0] = vals.q
@@ -106,7 +115,7 @@ def test_decode_fp8_parity(hq, hkv, d):
 
 def test_decode_step_fp8_stores_then_attends():
     lens = [300, 1, 77, 1024]
-    scales = np.float32([[0.03, 0.02]])
+    scales = np.float32([[0.03, 2.0 ** -6]])
     b, vals, kc, vc = fp8_batch(620, 32, 8, 128, lens, scales)
     qd = to_dev(vals.q, torch.bfloat16)
     kn = to_dev(vals.k_new, torch.bfloat16)
@@ -158,7 +167,7 @@ def test_b1_32k_fp8():
 def test_prefill_fp8_parity(hq, hkv, d, causal):
     lens = np.array([300, 70, 1, 129, 700, 64, 5])
     n_new = np.array([64, 70, 1, 33, 200, 0, 5])
-    scales = np.float32([[0.02, 0.015]])
+    scales = np.float32([[0.02, 2.0 ** -6]])
     b = W.custom(f"fp8_prefill_{hq}_{d}", n_layers=1, n_slots=4096, n_q_heads=hq, n_kv_heads=hkv,
                  head_dim=d, dtype="bf16", seq_lens=lens, n_new=n_new, seed=640 + hq + d)
     vals = W.host_values(b, 641 + d, poison_unreferenced=True)
@@ -189,7 +198,7 @@ def test_cascade_fp8_parity(hq, hkv, d):
     lens = [1100, 1025, 1024, 40, 300, 300, 777, 2000]
     groups = [[0, 1, 2], [3], [4, 5]]
     P = [1024, 33, 0]
-    scales = np.float32([[0.02, 0.01]])
+    scales = np.float32([[0.02, 2.0 ** -7]])
     b = shared_batch(f"fp8_cascade{hq}", lens, groups, P, 650, hq, hkv, d)
     vals = W.host_values(b, 651)
     kc, vc = O.quantize(vals.k_pool, scales[0, 0]), O.quantize(vals.v_pool, scales[0, 1])
@@ -204,3 +213,35 @@ def test_cascade_fp8_parity(hq, hkv, d):
     ref = O.decode_attention_fp8(vals.q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
                                  b.seq_lens, b.scale)
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 cascade g={hq // hkv} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("interleaved", [True, False])
+def test_rope_kv_store_fp8(d, interleaved):
+    from tests.test_gpu_rope import compare_rounded
+    rng = np.random.default_rng(660 + d + interleaved)
+    T, hq, hkv, n_slots, max_pos = 37, 8, 2, 200, 4096
+    q = W.normal_values((T, hq, d), 661, "bf16")
+    k = (W.normal_values((T, hkv, d), 662, "bf16") * 4).astype(np.float32)  # some saturate
+    v = W.normal_values((T, hkv, d), 663, "bf16")
+    kp = rng.choice(FINITE, size=(2, n_slots, hkv, d)).astype(np.uint8)
+    vp = rng.choice(FINITE, size=(2, n_slots, hkv, d)).astype(np.uint8)
+    pos = rng.integers(0, max_pos, size=T).astype(np.int32)
+    loc = rng.permutation(n_slots)[:T].astype(np.int32)
+    loc[5], loc[9] = -1, n_slots  # skipped
+    scales = np.float32([[1.0, 1.0], [0.03, 0.02]])
+    tab = W.rope_freqs_cis(max_pos, d)
+    kd, vd = to_dev(kp), to_dev(vp)
+    qd = to_dev(q, torch.bfloat16)
+    q_out = torch.empty_like(qd)
+    ops.rope_kv_store(kd, vd, 1, to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(pos),
+                      to_dev(tab), to_dev(loc), q=qd, q_out=q_out, interleaved=interleaved,
+                      kv_scales=to_dev(scales))
+    torch.cuda.synchronize()
+    q_ref, kc, vc = O.rope_kv_store_fp8(q, k, v, pos, tab, kp, vp, 1,
+                                        np.where(loc < n_slots, loc, -1), scales, interleaved)
+    got_k, got_v = kd.cpu().numpy(), vd.cpu().numpy()
+    say(f"  rope fp8 d={d} interleaved={interleaved}: {int((got_k != kc).sum())} K / "
+        f"{int((got_v != vc).sum())} V code mismatches")
+    assert np.array_equal(got_k, kc) and np.array_equal(got_v, vc)
+    compare_rounded(q_out.float().cpu().numpy(), q_ref, "bf16", "rotated q")
