@@ -339,6 +339,71 @@ class DecodeBench:
                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
 
 
+def _time_calls(fn, steps: int) -> float:
+    """Average ms of fn() over `steps` back-to-back calls between two events."""
+    import torch
+
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def new_token_steps(steps: int) -> dict:
+    """The steps upstream of attention on the new tokens of the packed-prefill
+    workload (T = 6710 tokens, 32 q / 8 KV heads, head_dim 128, bf16): the
+    store of their K/V rows (a2) and the fused RoPE + store (f1, q rotated in
+    place), and the same store into an E4M3 pool (quantising). GB/s counts the
+    bytes each call must move: new rows read, pool rows written, q read and
+    written."""
+    import torch
+
+    from paged_kv_cache_184_amd import ops
+    from paged_kv_cache_184_amd import workloads as W
+
+    b = W.packed_prefill(n_layers=1)
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(184_030)
+    T, hq, hkv, d = b.total_q, b.n_q_heads, b.n_kv_heads, b.head_dim
+    shape = (1, b.n_slots, hkv, d)
+    kp = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros_like(kp)
+    kp8 = torch.zeros(shape, dtype=torch.uint8, device=dev)
+    vp8 = torch.zeros_like(kp8)
+    scales = torch.full((1, 2), 1.0 / 64, dtype=torch.float32, device=dev)
+    q = torch.randn((T, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn((T, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((T, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    loc = torch.from_numpy(np.concatenate([
+        b.req_to_token[b.req_pool_indices[i], int(b.seq_lens[i] - b.n_new[i]):int(b.seq_lens[i])]
+        for i in range(b.batch)]).astype(np.int32)).to(dev)
+    pos = torch.from_numpy(np.concatenate([
+        np.arange(int(b.seq_lens[i] - b.n_new[i]), int(b.seq_lens[i]))
+        for i in range(b.batch)]).astype(np.int32)).to(dev)
+    tab = torch.from_numpy(W.rope_freqs_cis(8192, d)).to(dev)
+    row = hkv * d * 2  # bytes of one token's K (or V) row in bf16
+    out = {}
+    ms = _time_calls(lambda: ops.kv_store(kp, vp, 0, kn, vn, loc), steps)
+    out["kv_store_us"] = round(ms * 1e3, 2)
+    out["kv_store_gbs"] = round(4 * T * row / (ms * 1e-3) / 1e9, 1)
+    ms = _time_calls(lambda: ops.rope_kv_store(kp, vp, 0, kn, vn, pos, tab, loc, q=q), steps)
+    out["rope_kv_store_us"] = round(ms * 1e3, 2)
+    out["rope_kv_store_gbs"] = round((4 * T * row + 2 * T * hq * d * 2) / (ms * 1e-3) / 1e9, 1)
+    ms = _time_calls(lambda: ops.kv_store(kp8, vp8, 0, kn, vn, loc, kv_scales=scales), steps)
+    out["kv_store_fp8_us"] = round(ms * 1e3, 2)
+    out["kv_store_fp8_gbs"] = round((2 * T * row + T * row) / (ms * 1e-3) / 1e9, 1)
+    out["tokens"] = int(T)
+    return out
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
 
 
@@ -600,6 +665,8 @@ def main():
             del db
             torch.cuda.empty_cache()
     if not args.no_prefill:
+        detail["new_token_steps"] = new_token_steps(max(20, args.steps // 4))
+        print(f"# new-token steps: {detail['new_token_steps']}", file=sys.stderr, flush=True)
         pb = PrefillBench(n_layers=8, seed=184_004)
         p_step, p_attn = pb.run(max(10, args.steps // 5), 3)
         tflops = pb.flops() / (p_attn * 1e-3) / 1e12
