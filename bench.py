@@ -145,7 +145,8 @@ class DecodeBench:
         if split_tokens > 0:
             self.split = ops.split_cfg(max(1, -(-ctx // split_tokens)), 0, split_tokens)
         else:
-            self.split = ops.choose_split(ctx, b.batch, b.n_kv_heads)
+            self.split = ops.choose_split(ctx, b.batch, b.n_kv_heads,
+                                          total_len=int(b.seq_lens.sum()))
         max_splits = self.split.max_splits
         self.ws = ops.alloc_decode_workspace(B, b.n_q_heads, b.head_dim, max_splits)
         self.out = torch.empty_like(self.q)
