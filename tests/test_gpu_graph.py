@@ -7,7 +7,8 @@ split-KV attention with its merge. Between replays only device buffers change
 (seq_lens += 1, positions, the new tokens' q / k / v), as an engine keeps
 fixed-capacity metadata and rewrites it every step. Every replay must match the
 same calls run eagerly on a twin of the state, bit for bit (outputs and both
-pools), and the oracle within tolerance.
+pools), and the oracle within tolerance. Run for bf16 pools and for E4M3 code
+pools (quantising RoPE store, per-layer scales read by the kernels at run time).
 """
 
 import numpy as np
@@ -27,7 +28,7 @@ STEPS = 5
 class StepState:
     """Device buffers of one decode step whose addresses stay fixed."""
 
-    def __init__(self, b, vals, r2t, tab, split, ws_slots):
+    def __init__(self, b, vals, r2t, tab, split, kv="bf16", scales=None):
         dt = torch.bfloat16
         self.b = b
         self.r2t = torch.from_numpy(r2t).to(DEV)
@@ -37,8 +38,14 @@ class StepState:
         self.q = torch.empty((b.batch, b.n_q_heads, b.head_dim), dtype=dt, device=DEV)
         self.k_new = torch.empty((b.batch, b.n_kv_heads, b.head_dim), dtype=dt, device=DEV)
         self.v_new = torch.empty_like(self.k_new)
-        self.k_pool = torch.from_numpy(vals.k_pool).to(DEV, dt)
-        self.v_pool = torch.from_numpy(vals.v_pool).to(DEV, dt)
+        if kv == "fp8":
+            self.kv_scales = torch.from_numpy(scales).to(DEV)
+            self.k_pool = torch.from_numpy(O.quantize(vals.k_pool, scales[0, 0])).to(DEV)
+            self.v_pool = torch.from_numpy(O.quantize(vals.v_pool, scales[0, 1])).to(DEV)
+        else:
+            self.kv_scales = None
+            self.k_pool = torch.from_numpy(vals.k_pool).to(DEV, dt)
+            self.v_pool = torch.from_numpy(vals.v_pool).to(DEV, dt)
         self.tab = torch.from_numpy(tab).to(DEV)
         self.kv_indptr = torch.empty(b.batch + 1, dtype=torch.int32, device=DEV)
         self.loc = torch.empty(b.batch, dtype=torch.int32, device=DEV)
@@ -51,9 +58,10 @@ class StepState:
             ops.prepare_metadata(self.meta, ops.PKV_MODE_DECODE, split, self.kv_indptr, self.loc,
                                  self.splits),
             lambda: ops.rope_kv_store(self.k_pool, self.v_pool, 0, self.k_new, self.v_new,
-                                      self.pos, self.tab, self.loc, q=self.q),
+                                      self.pos, self.tab, self.loc, q=self.q,
+                                      kv_scales=self.kv_scales),
             ops.prepare_decode(self.q, self.k_pool, self.v_pool, 0, self.meta, b.scale, split,
-                               self.ws, self.out, stage="all"),
+                               self.ws, self.out, stage="all", kv_scales=self.kv_scales),
         ]
 
     def run(self):
@@ -69,7 +77,13 @@ class StepState:
         self.v_new.copy_(v)
 
 
-def test_decode_step_graph_replay_with_in_place_metadata():
+def same_bits(x, y):
+    return torch.equal(x.view(torch.int16), y.view(torch.int16)) if x.dtype == torch.bfloat16 \
+        else torch.equal(x, y)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_step_graph_replay_with_in_place_metadata(kv):
     # ragged lengths with room for STEPS more tokens per request
     lens0 = np.array([700, 33, 1500, 255, 16, 900, 64, 1201])
     b = W.custom("graph_steps", n_layers=1, n_slots=1 << 14, n_q_heads=32, n_kv_heads=8,
@@ -88,8 +102,9 @@ def test_decode_step_graph_replay_with_in_place_metadata():
     tab = W.rope_freqs_cis(int(lens0.max()) + STEPS + 1, 128)
     split = ops.split_cfg(8, 0, 256)
 
-    A = StepState(b, vals, r2t, tab, split, None)
-    B = StepState(b, vals, r2t, tab, split, None)
+    scales = np.float32([[0.02, 2.0 ** -6]])
+    A = StepState(b, vals, r2t, tab, split, kv, scales)
+    B = StepState(b, vals, r2t, tab, split, kv, scales)
     inputs = []
     for s in range(STEPS + 1):
         inputs.append(tuple(torch.from_numpy(W.normal_values(shape, 410 + 3 * s + j, "bf16"))
@@ -112,7 +127,7 @@ def test_decode_step_graph_replay_with_in_place_metadata():
     torch.cuda.synchronize()
 
     for step in range(STEPS):
-        say(f"graph step {step}")
+        say(f"graph step {step} ({kv})")
         if step > 0:
             qs, ks, vs = inputs[step]
             A.advance(qs, ks, vs)
@@ -123,8 +138,7 @@ def test_decode_step_graph_replay_with_in_place_metadata():
         torch.cuda.synchronize()
         assert torch.equal(A.out.view(torch.int16), B.out.view(torch.int16)), step
         assert torch.equal(A.loc, B.loc) and torch.equal(A.kv_indptr, B.kv_indptr), step
-        assert torch.equal(A.k_pool.view(torch.int16), B.k_pool.view(torch.int16)), step
-        assert torch.equal(A.v_pool.view(torch.int16), B.v_pool.view(torch.int16)), step
+        assert same_bits(A.k_pool, B.k_pool) and same_bits(A.v_pool, B.v_pool), step
         _ = (A.q.float() * 2).sum().item()  # unrelated eager work between replays
         # index step against the oracle, bit-exact
         lens = lens0 + step
@@ -133,8 +147,13 @@ def test_decode_step_graph_replay_with_in_place_metadata():
                               O.decode_locations(r2t, b.req_pool_indices, lens))
         if step in (0, STEPS - 1):
             # attention against the oracle on the device pools (rotated q as input)
-            kp = A.k_pool.float().cpu().numpy()
-            vp = A.v_pool.float().cpu().numpy()
-            ref = O.decode_attention(A.q.float().cpu().numpy(), kp, vp, 0, r2t,
-                                     b.req_pool_indices, lens, b.scale)
-            compare(A.out.float().cpu().numpy(), ref, "bf16", f"graph step {step}")
+            if kv == "fp8":
+                ref = O.decode_attention_fp8(A.q.float().cpu().numpy(), A.k_pool.cpu().numpy(),
+                                             A.v_pool.cpu().numpy(), scales, 0, r2t,
+                                             b.req_pool_indices, lens, b.scale)
+            else:
+                kp = A.k_pool.float().cpu().numpy()
+                vp = A.v_pool.float().cpu().numpy()
+                ref = O.decode_attention(A.q.float().cpu().numpy(), kp, vp, 0, r2t,
+                                         b.req_pool_indices, lens, b.scale)
+            compare(A.out.float().cpu().numpy(), ref, "bf16", f"graph step {step} ({kv})")
