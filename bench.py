@@ -556,7 +556,7 @@ def cpu_baseline(db: DecodeBench, seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this library is measured on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
 
