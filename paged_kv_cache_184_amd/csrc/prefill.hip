@@ -292,7 +292,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform: the LDS destinations of the transfers (M0) are then
+  // computed in scalar registers, not read back from a vector lane per transfer
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest work first
@@ -347,7 +349,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < Sg::NI; ++i) {
       const int rr = 16 * wave + Sg::RPI * i + prow;
-      off[i] = (int64_t)clamp_index(ids[rr], n_slots) * row_stride + 16 * chunk_of(rr);
+      // unsigned 32 x 32 -> 64-bit product (one multiply-add): the clamped
+      // slot is non-negative and the row stride is below 2^24 (at most 65535
+      // KV heads of 256 bytes)
+      off[i] = (int64_t)((uint64_t)(uint32_t)clamp_index(ids[rr], n_slots) * (uint32_t)row_stride +
+                         (uint32_t)(16 * chunk_of(rr)));
     }
   };
   // E4M3 pools: this lane's V chunks of the next block, in registers until
