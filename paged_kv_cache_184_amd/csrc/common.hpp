@@ -162,6 +162,13 @@ __host__ __device__ __forceinline__ int split_count(int L, int max_splits, int f
   return ceil_div(L, chunk);
 }
 
+// A word that every lane of the workgroup reads at the same address and that
+// no kernel writes while it runs (request lengths, row indices): loaded
+// through the scalar data cache, so several such loads are in flight at once.
+__device__ __forceinline__ int load_uniform(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 __device__ __forceinline__ int clamp_index(int x, int n) {
   // maps any int to [0, n): negatives to 0, too-large to n - 1
   return x < 0 ? 0 : (x >= n ? n - 1 : x);

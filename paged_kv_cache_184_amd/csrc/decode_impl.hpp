@@ -349,12 +349,13 @@ struct Plan {
 
 __host__ __device__ __forceinline__ int prefix_cap(int max_splits) { return max_splits / 2; }
 
-__device__ __forceinline__ Plan plan_for(const DecodeArgs& a, int b) {
+// The split plan from a request's raw seq_lens and prefix_len words (the
+// latter ignored without prefix lengths).
+__device__ __forceinline__ Plan plan_from(const DecodeArgs& a, int L_raw, int P_raw) {
   Plan p;
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+  const int L = L_raw < 0 ? 0 : (L_raw > a.stride ? (int)a.stride : L_raw);
   p.L = L;
-  int P = a.prefix_len ? a.prefix_len[b] : 0;
+  int P = a.prefix_len ? P_raw : 0;
   P = P < 0 ? 0 : (P > L ? L : P);
   p.P = P;
   int cap = a.split.max_splits;
@@ -366,6 +367,10 @@ __device__ __forceinline__ Plan plan_for(const DecodeArgs& a, int b) {
   }
   p.S = split_count(L - P, cap, a.split.fixed_splits, a.split.split_tokens, &p.chunk);
   return p;
+}
+
+__device__ __forceinline__ Plan plan_for(const DecodeArgs& a, int b) {
+  return plan_from(a, a.seq_lens[b], a.prefix_len ? a.prefix_len[b] : 0);
 }
 
 // What a split workgroup needs to know about its request and token range.
@@ -384,7 +389,17 @@ template <typename T, int D, int G, int NT>
 __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh, int s,
                                             SplitCtx& c) {
   constexpr int ROW = D * elem_size<T>::value;
-  const Plan p = plan_for(a, b);
+  // The request's length, prefix length and row index are scalar loads, all
+  // in flight before any is used: one memory round trip before the slot ids
+  // instead of three. Without prefix lengths the second load re-reads
+  // seq_lens[b].
+  int L_raw = load_uniform(a.seq_lens + b);
+  int P_raw = load_uniform((a.prefix_len ? a.prefix_len : a.seq_lens) + b);
+  int r_raw = load_uniform(a.req_pool_indices + b);
+  // an empty statement that takes the three words: every use comes after it,
+  // so the compiler cannot put a use (and its wait) between two of the loads
+  asm volatile("" : "+s"(L_raw), "+s"(P_raw), "+s"(r_raw));
+  const Plan p = plan_from(a, L_raw, P_raw);
   c.L = p.L;
   c.S = p.S;
   c.Sp = p.Sp;
@@ -399,7 +414,7 @@ __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh,
   }
   c.lo = p.P + s * c.chunk;
   c.hi = min(c.L, c.lo + c.chunk);
-  const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
+  const int r = clamp_index(r_raw, a.n_rows);
   c.row = a.req_to_token + (int64_t)r * a.stride;
   c.n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
   c.row_stride = (int64_t)a.n_kv_heads * ROW;

@@ -300,10 +300,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int tile = gridDim.x - 1 - blockIdx.x;  // longest work first
   const int t0 = tile * BQ;
 
-  const int q0 = a.qo_indptr[b];
-  int n_new = a.qo_indptr[b + 1] - q0;
+  // the request's words as scalar loads, all in flight before any is used
+  int q0 = load_uniform(a.qo_indptr + b);
+  int q1 = load_uniform(a.qo_indptr + b + 1);
+  int L = load_uniform(a.seq_lens + b);
+  int r_raw = load_uniform(a.req_pool_indices + b);
+  asm volatile("" : "+s"(q0), "+s"(q1), "+s"(L), "+s"(r_raw));
+  int n_new = q1 - q0;
   if (t0 >= n_new) return;
-  int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
   if (n_new > L) n_new = L;
   if (t0 >= n_new) return;
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int kv_full = a.causal ? P + t0 + 1 : L;     // keys every row of the tile sees
   const int nblk = (kv_end + kBK - 1) / kBK;
 
-  const int r = clamp_index(a.req_pool_indices[b], a.n_rows);
+  const int r = clamp_index(r_raw, a.n_rows);
   const int32_t* row = a.req_to_token + (int64_t)r * a.stride;
   const int n_slots = (int)(a.n_slots > 0x7fffffff ? 0x7fffffff : a.n_slots);
   const int64_t row_stride = (int64_t)a.n_kv_heads * Sg::ROW;
