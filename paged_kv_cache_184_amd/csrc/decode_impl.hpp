@@ -646,7 +646,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
 // (one memory round trip for up to 32 splits), the group's weights
 // w_s = l_s exp(m_s - M) are computed one split per lane and shared through
 // LDS, and the running stabiliser M is raised between groups (acc and the
-// weight sum rescaled), so the result is sum_s w_s o_s / sum_s w_s.
+// weight sum rescaled), so the result is sum_s w_s o_s / sum_s w_s. The first
+// group is loaded together with the request's length words, before the split
+// count is known: the workspace holds max_splits rows per head, and rows past
+// the count are replaced by zeros (their contents are stale) before use.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PER = D / 64;  // elements per lane
@@ -655,18 +658,33 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const Plan pl = plan_for(a, b);
+  const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
+  const float2* ml = (const float2*)(a.ml_part + 2 * part);
+  const float* o = a.o_part + part * D + lane * PER;
+  float ov[U][PER];
+  float2 mlv;
+  // rows c0 .. c0 + U - 1 (clamped to the workspace) and this lane's (m, l)
+  auto load_group = [&](int c0, int last) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) ov[u][e] = o[(int64_t)min(c0 + u, last) * D + e];
+    mlv = ml[min(c0 + lane, last)];
+  };
+  load_group(0, a.split.max_splits - 1);
+  int L_raw = load_uniform(a.seq_lens + b);
+  int P_raw = load_uniform((a.prefix_len ? a.prefix_len : a.seq_lens) + b);
+  // the group's loads stay above this point; the plan's first use stays below
+  asm volatile("" : "+s"(L_raw), "+s"(P_raw)::"memory");
+  const Plan pl = plan_from(a, L_raw, P_raw);
   const int S = pl.Sp + pl.S;  // prefix splits first, then the suffix splits
   // After the partial kernel ran with an output, requests without prefix
   // splits and with 0 or 1 suffix split are already written.
   if (a.merge_multi_only && pl.Sp == 0 && pl.S <= 1) return;
-  const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
-  const float2* ml = (const float2*)(a.ml_part + 2 * part);
-  const float* o = a.o_part + part * D + lane * PER;
   const int64_t orow = ((int64_t)b * a.n_q_heads + h) * D + lane * PER;
   if (S <= 1) {  // no split: zeros; one split: its normalised output is the result
 #pragma unroll
-    for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, S == 1 ? o[e] : 0.f);
+    for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, S == 1 ? ov[0][e] : 0.f);
     return;
   }
   float M = -INFINITY, den = 0.f;
@@ -675,13 +693,13 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   for (int c0 = 0; c0 < S; c0 += U) {
     const int n = min(U, S - c0);
-    float ov[U][PER];
+    if (c0 > 0) load_group(c0, S - 1);
+    // drop what lies past the request's splits (zero weight, zero row)
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < PER; ++e) ov[u][e] = o[(int64_t)(c0 + min(u, n - 1)) * D + e];
-    float2 mlv = make_float2(-INFINITY, 0.f);
-    if (lane < n) mlv = ml[c0 + lane];
+      for (int e = 0; e < PER; ++e) ov[u][e] = u < n ? ov[u][e] : 0.f;
+    if (lane >= n) mlv = make_float2(-INFINITY, 0.f);
     const float Mn = fmaxf(M, wave_max(mlv.x));  // finite: the group is not empty
     const float r = __builtin_amdgcn_exp2f((M - Mn) * kLog2e);  // 0 on the first group
     M = Mn;
