@@ -203,6 +203,26 @@ def test_padded_rows_and_poisoned_workspace():
     compare(o, ref, "bf16", "padded rows")
 
 
+def test_merge_ignores_stale_rows_past_split_count():
+    """The merge loads a group of partial rows before it knows the request's
+    split count; rows past the count (NaN here: the workspace is filled with
+    0xFF bytes) must not reach the result. Split counts 3, 7, 38 (two groups of
+    32) and 1 under a cap of 48."""
+    b = W.custom("stale", n_layers=1, n_slots=4096, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                 dtype="bf16", seq_lens=[40, 100, 600, 16], n_new=[1, 1, 1, 1], seed=95)
+    vals = W.host_values(b, 96)
+    db = DeviceBatch(b, vals)
+    store_new_tokens(db, 0)
+    ref, _, _ = oracle_after_store(b, vals, 0)
+    split = ops.split_cfg(48, 0, 16)
+    S, _ = O.split_plan(b.seq_lens, split.max_splits, split.fixed_splits, split.split_tokens)
+    assert list(S) == [3, 7, 38, 1]
+    out, _ = run_decode(db, 0, split, ws_fill=255)
+    o = out.float().cpu().numpy()
+    assert np.isfinite(o).all()
+    compare(o, ref, "bf16", "stale workspace rows")
+
+
 def test_recycled_request_rows():
     """A second generation reuses the request rows with shorter lengths; the
     stale table entries past the new lengths hold live slots of the old
