@@ -88,8 +88,8 @@ __device__ __forceinline__ void load_tile(TileBuf<T, D, LPR>& buf, const char* k
     const int64_t off = (int64_t)slot[j] * row_stride;
 #pragma unroll
     for (int k = 0; k < Geo<T, D, LPR>::CH; ++k) {
-      buf.k[j][k] = *(const u32x4*)(kbase + off + 16 * LPR * k);
-      buf.v[j][k] = *(const u32x4*)(vbase + off + 16 * LPR * k);
+      buf.k[j][k] = load_stream(kbase + off + 16 * LPR * k);
+      buf.v[j][k] = load_stream(vbase + off + 16 * LPR * k);
     }
   }
 }
