@@ -106,7 +106,8 @@ __device__ __forceinline__ void prefix_split(const DecodeArgs& a, int kvh, int s
   const float vscale = kFp8 ? a.kv_scale[1] : 1.f;
   WaveState<D, 1> st;
   init_state(st);
-  wave_loop<D, 1, KV>(st, slot_lds[wave], vs0[wave], row, n_slots, wlo, whi, qf, kbase, vbase,
+  // the column tiles of a group re-read these rows: default cache policy
+  wave_loop<D, 1, KV, false>(st, slot_lds[wave], vs0[wave], row, n_slots, wlo, whi, qf, kbase, vbase,
                       row_stride, a.scale * kLog2e * kscale, lane);
 
   // Hand the wave's (m, l, O) per column to LDS (O rows into the wave's own V

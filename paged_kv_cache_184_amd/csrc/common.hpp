@@ -162,13 +162,14 @@ __host__ __device__ __forceinline__ int split_count(int L, int max_splits, int f
   return ceil_div(L, chunk);
 }
 
-// K/V row bytes of the VALU decode kernel, read with the non-temporal cache
-// policy. Each instruction there covers whole 128-byte lines of a row, and the
-// bytes are read once unless requests share slots: measured 5-8% shorter
-// launches at 16K-32K contexts and on ragged batches, but 16% longer with 32
-// requests over one 4096-token prefix, the case cascade decode serves. The
-// MFMA decode kernel keeps the default policy: it reads each line with two
-// half-line instructions, and streaming made its large batches 6-8% slower.
+// K/V row bytes that a decode launch reads once, with the non-temporal cache
+// policy, wherever one load instruction covers whole 128-byte lines: both
+// rows in the VALU decode kernel, the V rows in the MFMA one. Measured:
+// 5-11% shorter launches at 16K-32K contexts and on ragged batches, but 16%
+// longer with 32 requests over one 4096-token prefix under plain attention,
+// the case cascade decode serves. The MFMA kernel's K fragments read each line
+// with two half-line instructions and keep the default policy (streaming them
+// made large batches 6-8% slower).
 __device__ __forceinline__ u32x4 load_stream(const char* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }

@@ -131,8 +131,9 @@ __device__ __forceinline__ void init_state(WaveState<D, NTC>& st) {
 // Loads of block i of a super-block into registers: K fragments, and V in
 // the layout its LDS tile is written in (lane l of row group t holds row
 // RPI t + l / CPR, physical chunk l % CPR). Positions past ce re-read the
-// last valid token.
-template <int D, typename KV = bf16_t>
+// last valid token. kStreamV: V rows (whole lines per load) take the streaming
+// policy; launches that re-read the same rows keep the default.
+template <int D, typename KV = bf16_t, bool kStreamV = true>
 __device__ __forceinline__ void issue_block(KBlock<D, KV>& kb, const int* slots, int i, int cb,
                                             int ce, const char* kbase, const char* vbase,
                                             int64_t row_stride, int lane) {
@@ -156,7 +157,7 @@ __device__ __forceinline__ void issue_block(KBlock<D, KV>& kb, const int* slots,
       const int r = Gm::RPI * t + prow;
       const int lch = pch ^ (r & (Gm::CPR - 1));
       const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
-      kb.v[t] = *(const u32x4*)(vbase + off + 16 * lch);
+      kb.v[t] = kStreamV ? load_stream(vbase + off + 16 * lch) : *(const u32x4*)(vbase + off + 16 * lch);
     }
   } else {
     // lane l of load t: row RPI t + l / CPR, code chunk l % CPR
@@ -164,7 +165,8 @@ __device__ __forceinline__ void issue_block(KBlock<D, KV>& kb, const int* slots,
     for (int t = 0; t < Ld::NV; ++t) {
       const int r = Ld::RPI * t + lane / Ld::CPR;
       const int64_t off = (int64_t)slots[min(kBlk * i + r, last)] * row_stride;
-      kb.v[t] = *(const u32x4*)(vbase + off + 16 * (lane % Ld::CPR));
+      const char* p = vbase + off + 16 * (lane % Ld::CPR);
+      kb.v[t] = kStreamV ? load_stream(p) : *(const u32x4*)p;
     }
   }
 }
@@ -272,7 +274,7 @@ __device__ __forceinline__ void compute_block(WaveState<D, NTC>& st, const KBloc
 // NB consecutive 32-key blocks of one super-block, straight-line: block i's
 // loads are issued kRing - 1 blocks before its compute, into ring entry
 // i % kRing.
-template <int D, int NTC, int NB, typename KV = bf16_t>
+template <int D, int NTC, int NB, typename KV = bf16_t, bool kStreamV = true>
 __device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, const int* slots,
                                           int cb, int ce, const u32x4 (&qf)[NTC][MGeo<D>::KS],
                                           const char* kbase, const char* vbase,
@@ -280,12 +282,13 @@ __device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, c
   KBlock<D, KV> kb[kRing];
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j)
-    if (j < NB) issue_block<D, KV>(kb[j], slots, j, cb, ce, kbase, vbase, row_stride, lane);
+    if (j < NB)
+      issue_block<D, KV, kStreamV>(kb[j], slots, j, cb, ce, kbase, vbase, row_stride, lane);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     if (i + kRing - 1 < NB)
-      issue_block<D, KV>(kb[(i + kRing - 1) % kRing], slots, i + kRing - 1, cb, ce, kbase, vbase,
-                         row_stride, lane);
+      issue_block<D, KV, kStreamV>(kb[(i + kRing - 1) % kRing], slots, i + kRing - 1, cb, ce,
+                                   kbase, vbase, row_stride, lane);
     // keep the later blocks' loads ahead of this block's MFMAs
     __builtin_amdgcn_sched_barrier(0);
     compute_block<D, NTC, KV>(st, kb[i % kRing], vstage, qf, scale2, cb + kBlk * i, whi, lane);
@@ -295,7 +298,7 @@ __device__ __forceinline__ void block_run(WaveState<D, NTC>& st, char* vstage, c
 // A wave's contiguous key range [wlo, whi) of one request row, in 128-key
 // super-blocks: the slot ids of each are staged in this wave's LDS row (the
 // next super-block's prefetched into registers meanwhile).
-template <int D, int NTC, typename KV = bf16_t>
+template <int D, int NTC, typename KV = bf16_t, bool kStreamV = true>
 __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, char* vtile,
                                           const int32_t* row, int n_slots, int wlo, int whi,
                                           const u32x4 (&qf)[NTC][MGeo<D>::KS], const char* kbase,
@@ -322,8 +325,8 @@ __device__ __forceinline__ void wave_loop(WaveState<D, NTC>& st, int* slots, cha
 #define PKV_DM_RUN(n)                                                                          \
   case n:                                                                                      \
     if constexpr (n <= kSB)                                                                    \
-      block_run<D, NTC, n, KV>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, scale2, \
-                               whi, lane);                                                     \
+      block_run<D, NTC, n, KV, kStreamV>(st, vtile, slots, cb, ce, qf, kbase, vbase, row_stride, \
+                                         scale2, whi, lane);                                   \
     break;
       PKV_DM_RUN(1) PKV_DM_RUN(2) PKV_DM_RUN(3) PKV_DM_RUN(4)
       PKV_DM_RUN(5) PKV_DM_RUN(6) PKV_DM_RUN(7) PKV_DM_RUN(8)
