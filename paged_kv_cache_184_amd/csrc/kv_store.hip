@@ -52,8 +52,10 @@ __global__ __launch_bounds__(256) void kv_store_fp8_kernel(
   const float vs = kv_scale[1];
   const u32x4 a = quant_bf16x16(*(const u32x4*)(kn + src), *(const u32x4*)(kn + src + 16), ks);
   const u32x4 b = quant_bf16x16(*(const u32x4*)(vn + src), *(const u32x4*)(vn + src + 16), vs);
-  *(u32x4*)(k + dst) = a;
-  *(u32x4*)(v + dst) = b;
+  // code rows are not read again by this launch: streaming stores (measured
+  // 9% shorter; the bf16 store and the RoPE store measured slower with them)
+  __builtin_nontemporal_store(a, (u32x4*)(k + dst));
+  __builtin_nontemporal_store(b, (u32x4*)(v + dst));
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p16, uint8_t* __restrict__ tail,
