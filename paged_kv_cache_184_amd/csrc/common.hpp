@@ -125,6 +125,23 @@ constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7-i within 8
 constexpr int kRowMirror = 0x140;   // row_mirror: lane i <-> 15-i within 16
 constexpr int kRowRor8 = 0x128;     // row_ror:8: lane i <- lane (i+8) mod 16
 
+// x plus the value of lane l ^ 16 (add_xor16) or lane l ^ 32 (add_xor32), by
+// the gfx950 row-swap instructions: a VALU exchange instead of an LDS permute.
+// With both operands equal to x, v_permlane16_swap leaves (x of the even row,
+// x of the odd row) of each row pair in its two results, and v_permlane32_swap
+// (x of lanes 0-31, x of lanes 32-63); their sum is own + partner in either
+// order, which is the same bits (fp addition is commutative).
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over each aligned group of 8 lanes; every lane of the group gets the
 // same bits (each step adds a commutative pair).
 __device__ __forceinline__ float sum8(float x) {
@@ -132,6 +149,18 @@ __device__ __forceinline__ float sum8(float x) {
   x += dpp<kQuadSwap2>(x);
   x += dpp<kHalfMirror>(x);
   return x;
+}
+
+// Sum over the wave with the same bits in every lane and the same bits as the
+// butterfly x += x[l ^ off] for off = 1, 2, ..., 32: after the first two steps
+// a quad holds one value, so the half-row mirror pairs it with the quad at
+// l ^ 4, and the row mirror then pairs each 8-lane half with the one at l ^ 8.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  return add_xor32(add_xor16(x));
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -582,9 +582,7 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s
   // (lanes c + LPR grp; with LPR = 8, row_ror:8 first pairs the groups of a row).
   auto over_groups = [&](float x) {
     if constexpr (LPR == 8) x += dpp<kRowRor8>(x);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    return add_xor32(add_xor16(x));
   };
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -718,9 +716,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
       for (int e = 0; e < PER; ++e) acc[e] = fmaf(wu, ov[u][e], acc[e]);
     }
   }
-  // sum of the weights over the wave (butterfly: every lane gets the same bits)
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off);
+  // sum of the weights over the wave (every lane gets the same bits)
+  den = wave_sum(den);
   const float inv = 1.0f / den;
 #pragma unroll
   for (int e = 0; e < PER; ++e) store_out<T>(a.out, orow + e, acc[e] * inv);
