@@ -423,38 +423,39 @@ __device__ __forceinline__ bool split_setup(const DecodeArgs& a, int b, int kvh,
 
 // Store of the new token (position L-1) of this KV head by the wave whose
 // share [wlo, whi) holds it, completed before that wave reads it back. FP8
-// pools take bf16 rows, quantised under the layer's K or V scale.
+// pools take bf16 rows, quantised under the layer's K or V scale. The slot id
+// and the new row are independent loads and are issued together; the caller
+// may have loads of its own in flight, which the final wait also covers.
 template <typename T, int D>
 __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const SplitCtx& c, int b,
                                                 int kvh, int wlo, int whi, int lane) {
-  constexpr int ROW = D * elem_size<T>::value;
+  constexpr int ES = elem_size<T>::value;
+  constexpr int ROW = D * ES;
   if (!a.k_new || c.L - 1 < wlo || c.L - 1 >= whi) return;
+  constexpr int CPR = ROW / 16;  // 16-byte chunks of one (slot, KV head) row of the pool
+  const bool mine = lane < 2 * CPR;
+  const bool is_k = lane < CPR;
+  const int chk = lane % CPR;
+  // a chunk of the pool row takes 16 bytes of the new row (bf16, f32) or 32
+  // (bf16 values quantised to 16 E4M3 codes)
+  constexpr int SRC = ES == 1 ? 32 : 16;
+  const char* src = (const char*)(is_k ? a.k_new : a.v_new) +
+                    ((int64_t)b * a.n_kv_heads + kvh) * (CPR * SRC) + SRC * chk;
+  u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+  if (mine) {
+    v0 = *(const u32x4*)src;
+    if constexpr (ES == 1) v1 = *(const u32x4*)(src + 16);
+  }
   const int raw = c.row[c.L - 1];
-  constexpr int CPR = ROW / 16;  // 16-byte chunks of one (slot, KV head) row
-  if constexpr (elem_size<T>::value == 1) {
-    if (raw >= 0 && raw < c.n_slots && lane < 2 * CPR) {
-      const int chk = lane % CPR;
-      const bool is_k = lane < CPR;
-      const char* src = (const char*)(is_k ? a.k_new : a.v_new) +
-                        ((int64_t)b * a.n_kv_heads + kvh) * (2 * ROW) + 32 * chk;
-      char* dst = (char*)(is_k ? a.k : a.v) + (int64_t)raw * c.row_stride + (int64_t)kvh * ROW +
-                  16 * chk;
-      *(u32x4*)dst = quant_bf16x16(*(const u32x4*)src, *(const u32x4*)(src + 16),
-                                   a.kv_scale[is_k ? 0 : 1]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    return;
+  if (raw >= 0 && raw < c.n_slots && mine) {
+    char* dst = (char*)(is_k ? a.k : a.v) + (int64_t)raw * c.row_stride + (int64_t)kvh * ROW +
+                16 * chk;
+    if constexpr (ES == 1)
+      *(u32x4*)dst = quant_bf16x16(v0, v1, a.kv_scale[is_k ? 0 : 1]);
+    else
+      *(u32x4*)dst = v0;
   }
-  if (raw >= 0 && raw < c.n_slots && lane < 2 * CPR) {
-    const int chk = lane % CPR;
-    const char* src = (const char*)(lane < CPR ? a.k_new : a.v_new) +
-                      ((int64_t)b * a.n_kv_heads + kvh) * ROW + 16 * chk;
-    char* dst = (char*)(lane < CPR ? a.k : a.v) + (int64_t)raw * c.row_stride +
-                (int64_t)kvh * ROW + 16 * chk;
-    *(u32x4*)dst = *(const u32x4*)src;
-  }
-  // the row is read back below by this same wave: complete the stores first
+  // the row is read back by this same wave: complete the stores first
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -529,8 +530,6 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s
   const int n_slots = sc.n_slots;
   const int64_t row_stride = sc.row_stride;
 
-  store_new_token<T, D>(a, sc, b, kvh, wlo, whi, lane);
-
   const char* kbase = (const char*)a.k + (int64_t)kvh * Gm::ROW + 16 * c;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Gm::ROW + 16 * c;
   // chunk k of this lane is row chunk c + LPR k
@@ -550,6 +549,9 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s
 #pragma unroll
     for (int k = 0; k < CH; ++k)
       q[h][k] = *(const u32x4*)(qbase + (int64_t)h * Gm::ROW + 16 * LPR * k);
+
+  // with the ids and q in flight, so that its wait overlaps them
+  store_new_token<T, D>(a, sc, b, kvh, wlo, whi, lane);
 
   const float scale2 = a.scale * kLog2e;
   State<T, D, G, LPR> st;
@@ -613,10 +615,12 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s
   finish_split<T, D, G, kWaves>(a, red_acc, wstride, red_ml, b, kvh, s, sc);
 }
 
-// One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B).
+// One workgroup per (request b, KV head, split s), grid (Hkv, max_splits, B),
+// plus one more row of splits (s = max_splits) when the index step is fused.
 // Optional fused steps:
-//   a.kv_indptr_out / loc_out / splits_out: workgroup (0, 0, 0) first runs the
-//     index step for the whole batch;
+//   a.kv_indptr_out / loc_out / splits_out: workgroup (0, max_splits, 0) runs
+//     the index step for the whole batch, beside the split workgroups (so no
+//     split waits for it) and the rest of that row exits at once;
 //   a.k_new / v_new: the wave whose share holds position L-1 first stores the
 //     new token's K/V row of this KV head at slot req_to_token[r_b, L-1]
 //     (skipped if that slot is out of range), then reads it like any other;
@@ -634,8 +638,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_partial_kernel(DecodeArgs 
   const int kvh = blockIdx.x;
   const int s = blockIdx.y;
   const int b = blockIdx.z;
-  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
-    index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
+  if (s == a.split.max_splits) {  // the index-step row
+    if (kvh == 0 && b == 0) index_step_block<64 * kWaves>(a, &slot_lds[0][0]);
+    return;
+  }
   decode_split<T, D, G>(a, kvh, s, b, slot_lds, &red_acc[0][0][0], G * D, red_ml);
 }
 
@@ -728,7 +734,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int MAXG = 16>
 hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
-  dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
+  dim3 grid(a.n_kv_heads, a.split.max_splits + (fuses_index_step(a) ? 1 : 0), a.batch);
   switch (g) {
     case 1: decode_partial_kernel<T, D, 1><<<grid, 64 * kWaves, 0, stream>>>(a); break;
     case 2: decode_partial_kernel<T, D, 2><<<grid, 64 * kWaves, 0, stream>>>(a); break;

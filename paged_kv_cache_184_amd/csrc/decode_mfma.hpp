@@ -411,8 +411,10 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
   const int kvh = blockIdx.x;  // KV head fastest: XCD-balanced (see decode_impl.hpp)
   const int s = blockIdx.y;
   const int b = blockIdx.z;
-  if ((a.kv_indptr_out || a.loc_out || a.splits_out) && s == 0 && kvh == 0 && b == 0)
-    index_step_block<64 * kW>(a, &slot_lds[0][0]);
+  if (s == a.split.max_splits) {  // the index-step row (see decode_partial_kernel)
+    if (kvh == 0 && b == 0) index_step_block<64 * kW>(a, &slot_lds[0][0]);
+    return;
+  }
   mfma_split<D, G, KV>(a, kvh, s, b, vs0, slot_lds, red_ml);
 }
 
@@ -421,7 +423,7 @@ __global__ __launch_bounds__(64 * kW, 2) void decode_mfma_kernel(DecodeArgs a) {
 template <int D, typename KV = bf16_t>
 hipError_t partials_for_dim(const DecodeArgs& a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
-  dim3 grid(a.n_kv_heads, a.split.max_splits, a.batch);
+  dim3 grid(a.n_kv_heads, a.split.max_splits + (fuses_index_step(a) ? 1 : 0), a.batch);
   if constexpr (sizeof(KV) == 1) {
     switch (g) {
       case 1: decode_mfma_kernel<D, 1, KV><<<grid, 64 * kW, 0, stream>>>(a); return hipGetLastError();

@@ -47,6 +47,12 @@ struct DecodeArgs {
   const float* kv_scale;
 };
 
+// Whether a partial-kernel launch also runs the index step (on one extra row
+// of split workgroups, beside the others).
+inline __host__ __device__ bool fuses_index_step(const DecodeArgs& a) {
+  return a.kv_indptr_out || a.loc_out || a.splits_out;
+}
+
 // Cascade decode partials: the groups' prefix splits and every request's own
 // (suffix) splits in one launch; the merge kernel follows.
 hipError_t launch_cascade_partials(const DecodeArgs& a, hipStream_t stream);
