@@ -263,6 +263,25 @@ def test_merge_alone_matches_full_call():
     assert torch.equal(full.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("hkv,g", [(16, 1), (16, 4), (32, 2), (16, 8)])
+def test_many_kv_heads_merge_placement(hkv, g):
+    """With Hkv a multiple of 8 the merge serves each q head on the XCD that
+    wrote its partials (a permutation of the merge grid): the output matches
+    the oracle and, bit for bit, the merge-only entry point, which keeps the
+    identity map. g = 8 runs the MFMA partial kernel."""
+    b = W.custom(f"hkv{hkv}g{g}", n_layers=1, n_slots=8192, n_q_heads=g * hkv, n_kv_heads=hkv,
+                 head_dim=128, dtype="bf16", seq_lens=[900, 40, 2500], n_new=[1] * 3,
+                 seed=150 + hkv + g)
+    split = ops.split_cfg(16, 0, 64)
+    db, _ = full_check(b, 151, [split])
+    full, ws = run_decode(db, 0, split)
+    out2 = torch.empty_like(full)
+    ops.decode_partials(db.q, db.k_pool, db.v_pool, 0, db.meta(), b.scale, split, ws)
+    ops.decode_merge(db.meta(), b.n_q_heads, b.head_dim, torch.bfloat16, split, ws, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), out2.view(torch.int16))
+
+
 def test_error_leaves_output_untouched():
     b = W.tiny_decode()
     vals = W.host_values(b, 130)
