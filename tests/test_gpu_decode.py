@@ -331,6 +331,40 @@ def test_decode_step_fused_matches_separate_calls(hq):
     compare(out.float().cpu().numpy(), ref, "bf16", "fused decode step")
 
 
+@pytest.mark.parametrize("hq", [16, 32])  # g = 4 (VALU kernel), g = 8 (MFMA kernel)
+def test_decode_step_at_split_cap(hq):
+    """The fused step with max_splits at its cap (PKV_MAX_SPLITS): the index step
+    runs on the grid row after the last split, so its outputs, the stored rows
+    and the attention must all still be exact; fixed splits above a request's
+    length leave most split workgroups without work."""
+    cap = ops._lib.PKV_MAX_SPLITS
+    b = W.custom(f"cap{hq}", n_layers=1, n_slots=8192, n_q_heads=hq, n_kv_heads=4, head_dim=128,
+                 dtype="bf16", seq_lens=[5000, 1, 300], n_new=[1] * 3, seed=160 + hq)
+    vals = W.host_values(b, 161)
+    split = ops.split_cfg(cap, 0, 16)
+    db1 = DeviceBatch(b, vals)
+    loc1 = store_new_tokens(db1, 0)
+    ref_out, _ = run_decode(db1, 0, split)
+    db2 = DeviceBatch(b, vals)
+    B = b.batch
+    ind = torch.full((B + 1,), -9, dtype=torch.int32, device=DEV)
+    loc = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    spl = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    ws = ops.alloc_decode_workspace(B, b.n_q_heads, b.head_dim, split.max_splits)
+    out = ops.decode_step(db2.q, db2.k_pool, db2.v_pool, 0, db2.meta(), b.scale, split, ws,
+                          k_new=db2.k_new, v_new=db2.v_new, kv_indptr_out=ind, loc_out=loc,
+                          splits_out=spl)
+    torch.cuda.synchronize()
+    assert np.array_equal(ind.cpu().numpy(), O.kv_indptr(b.seq_lens))
+    assert np.array_equal(loc.cpu().numpy(), loc1.cpu().numpy())
+    S, _ = O.split_plan(b.seq_lens, split.max_splits, split.fixed_splits, split.split_tokens)
+    assert np.array_equal(spl.cpu().numpy(), S)
+    assert torch.equal(db2.k_pool.view(torch.int16), db1.k_pool.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+    ref, _, _ = oracle_after_store(b, vals, 0)
+    compare(out.float().cpu().numpy(), ref, "bf16", "fused decode step at the split cap")
+
+
 def test_repeated_calls_and_shrinking_batch():
     """Repeated calls on one workspace, with the batch changing, stay exact."""
     b = W.custom("rep", n_layers=1, n_slots=1 << 16, n_q_heads=32, n_kv_heads=8, head_dim=128,
