@@ -25,7 +25,7 @@
 //     v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand for the whole tile);
 //   * softmax in base 2 with a per-row stabiliser that is raised only when a
-//     score exceeds it by more than kTau (tested on the raw row maxima; the
+//     score exceeds it by more than kTau (seen as a row sum above 2^kTau; the
 //     scale folds into the exponent's FMA); P is rounded to bf16 and the row
 //     sums are those rounded values summed by one more MFMA (a ones operand
 //     times P^T);
@@ -57,7 +57,9 @@ constexpr int kRows = 128;   // query rows per workgroup
 constexpr int kBK = 64;      // keys per block
 constexpr int kThreads = 256;
 constexpr int kStages = 2;
-constexpr float kTau = 64.0f;  // log2 headroom of the fixed stabiliser
+// log2 headroom of the fixed stabiliser (kTau = 64): a row sum above 2^kTau
+// flags the tile
+constexpr float kSumLimit = 0x1p64f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
@@ -136,18 +138,19 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 // masked score (-inf) gives weight 0.
 //
 // The stabiliser m of a row is fixed for the whole pass and O is never
-// rescaled here: m is set from the first 32 keys (init), and a later score
-// more than kTau above it only sets `bad` (the caller then recomputes the tile
-// with m = the exact row maxima, collected in mseen). With kTau = 64 the
-// weights stay below 2^64, so P, the row sums and O stay far from the fp32 /
-// bf16 range limit until `bad` is raised.
+// rescaled here: m is set from the first 32 keys (init). No row maximum is
+// taken after that: a later score more than kTau above m shows up as a row
+// sum above 2^kTau, which the caller checks once per tile before it
+// recomputes the tile with m = the exact row maxima (collected in mseen by a
+// TRACK pass). Below that limit the weights, the row sums and O stay far from
+// the fp32 / bf16 range limits.
 // MASK: the block straddles the causal diagonal or the sequence end (a
 // separate instantiation, so unmasked blocks carry no per-score selects).
-template <int D, int G, bool MASK, typename KV>
+template <int D, int G, bool MASK, typename KV, bool TRACK>
 __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
     const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
-    float (&m)[2], float (&mseen)[2], bool& bad, bool init, int k0,
+    float (&m)[2], float (&mseen)[2], bool init, int k0,
     const int (&limit)[2], float scale2, int lane) {
   using Gm = PGeo<D>;
   constexpr int KS = Gm::KSTEPS;
@@ -211,27 +214,27 @@ __device__ __forceinline__ void attend_block(
           for (int r = 0; r < 4; ++r) s[h][n][r] = 16 * h + r <= rel ? s[h][n][r] : -INFINITY;
       }
     }
-    float mx[2];
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    // this lane's raw row maxima of the half block, scaled (scale2 > 0: a
+    // fully masked lane keeps -inf)
+    auto row_max = [&](int n) {
       const float x = fmaxf(fmaxf(fmaxf(s[0][n][0], s[0][n][1]), fmaxf(s[0][n][2], s[0][n][3])),
                             fmaxf(fmaxf(s[1][n][0], s[1][n][1]), fmaxf(s[1][n][2], s[1][n][3])));
-      mx[n] = x * scale2;  // scale2 > 0: a fully masked lane keeps -inf
-    }
+      return x * scale2;
+    };
     if (init && j == 0) {
       // first 32 keys of the tile's first pass: the stabiliser is their row
       // maximum (key 0 is visible to every row, so it is finite); O and the
       // row sums are still zero, so nothing is rescaled
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        float x = fmaxf(mx[n], __shfl_xor(mx[n], 16));
+        const float mx = row_max(n);
+        float x = fmaxf(mx, __shfl_xor(mx, 16));
         m[n] = fmaxf(x, __shfl_xor(x, 32));
       }
     }
+    if constexpr (TRACK) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      mseen[n] = fmaxf(mseen[n], mx[n]);
-      bad |= mx[n] > m[n] + kTau;
+      for (int n = 0; n < 2; ++n) mseen[n] = fmaxf(mseen[n], row_max(n));
     }
     // P^T (bf16) in the B-operand layout: slots 0..3 = key tile 2j, 4..7 = tile 2j+1
     u32x4 pf[2];
@@ -436,11 +439,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   f32x4 lacc[2];
   float m[2] = {-INFINITY, -INFINITY};
   float mseen[2] = {-INFINITY, -INFINITY};
-  bool bad = false;
-  // Pass 0 fixes each row's stabiliser from its first 32 keys. Pass 1 runs only
-  // if some score of the tile rose more than kTau above it; it starts from the
-  // exact row maxima that pass 0 saw, so it cannot overflow.
-  for (int pass = 0;; ++pass) {
+  // One pass over the tile's keys. With init_pass, each row's stabiliser is
+  // fixed from its first 32 keys; with track, the exact row maxima are
+  // gathered in mseen (that pass's O and row sums are not used).
+  auto run_pass = [&](auto track, bool init_pass) {
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt) {
       o[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -448,7 +450,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     }
     lacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
     lacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool first_pass = pass == 0;
 
     // Transfer order per wave, kept identical in every iteration so that the
     // explicit wait counts are exact: before block i is computed the queue
@@ -482,9 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       offsets(u ^ 1, off);
       issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
       const char* st = stage_ptr(u);
-      attend_block<D, G, decltype(masked)::value, KV>(st, st + Sg::KTILE, qf, o, lacc, m, mseen,
-                                                      bad, first_pass && i == 0, i * kBK, limit,
-                                                      scale2, lane);
+      attend_block<D, G, decltype(masked)::value, KV, decltype(track)::value>(
+          st, st + Sg::KTILE, qf, o, lacc, m, mseen, init_pass && i == 0, i * kBK, limit, scale2,
+          lane);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
     // Blocks that every row sees whole and that end inside the sequence need
@@ -502,18 +503,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         block(i0 + u, u, std::true_type{});
       }
     }
-    // drain the transfers still in flight (before a second pass or the exit)
+    // drain the transfers still in flight (before another pass or the exit)
     __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
-    if (!first_pass) break;
-    // workgroup-wide decision; the barrier also frees the stages for pass 1
-    if (lane == 0) redo[wave] = __builtin_amdgcn_ballot_w64(bad) != 0;
-    __syncthreads();
-    if (!(redo[0] | redo[1] | redo[2] | redo[3])) break;
+  };
+  run_pass(std::false_type{}, true);
+  // A score more than kTau above its row's stabiliser gives a weight above
+  // 2^kTau, so that row's sum (of the same rounded weights) exceeds 2^kTau or
+  // is not finite. Such a tile is done again: one pass gathers the exact row
+  // maxima, the last one uses them as the stabiliser and cannot overflow.
+  bool bad = false;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) bad |= !(lacc[n][0] <= kSumLimit);
+  // workgroup-wide decision; the barrier also frees the stages for the next pass
+  if (lane == 0) redo[wave] = __builtin_amdgcn_ballot_w64(bad) != 0;
+  __syncthreads();
+  if (redo[0] | redo[1] | redo[2] | redo[3]) {
+    run_pass(std::true_type{}, false);
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       float x = fmaxf(mseen[n], __shfl_xor(mseen[n], 16));
       m[n] = fmaxf(x, __shfl_xor(x, 32));
     }
+    __syncthreads();  // the stages are free for the last pass
+    run_pass(std::false_type{}, false);
   }
 
 #pragma unroll
