@@ -564,9 +564,16 @@ def cpu_baseline(db: DecodeBench, seconds: float):
         if el >= seconds:
             break
     gbs = db.kv_bytes() * reps / el / 1e9
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "host_cpus_usable": affinity,
+            "blas_threads": int(threads),
             "sample": f"{reps} full oracle decode calls (B=1, ctx {db.b.seq_lens[0]}, 32 q heads) "
-                      f"in {el:.1f} s; BLAS threads as reported by threadpoolctl"}
+                      f"in {el:.1f} s; cores = BLAS threads (threadpoolctl), the only "
+                      f"multi-threaded part of the oracle"}
 
 
 def main():

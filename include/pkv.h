@@ -138,6 +138,27 @@ typedef struct pkv_split_cfg {
   int32_t reserved;
 } pkv_split_cfg;
 
+/* The library's default split configuration for a decode batch, the one its
+ * own measurements use (P2, bullet on keeping tuning constants in one place;
+ * P1, bullet on the B=1 decode latency across 1K-32K contexts). A host-only
+ * computation: no device access, safe to call without a GPU.
+ *   max_len     longest seq_len of the batch (>= 0)
+ *   batch       requests (>= 1)
+ *   total_len   sum of the batch's seq_lens, or a negative value when unknown
+ *   n_kv_heads  KV heads of the pool (>= 1)
+ *   n_cu        compute units of the device (>= 1; 256 on MI355X)
+ * Rule: one request, or a batch without total_len, takes tokens per split
+ * T = ceil(max_len / max(1, n_cu / (batch * n_kv_heads))), so that the
+ * (request, KV head, split) workgroups cover the device about once; a batch
+ * with total_len takes T = ceil(total_len * n_kv_heads / (2 * n_cu)), about
+ * two workgroups per compute unit. T is rounded up to a multiple of
+ * PKV_SPLIT_ALIGN and clamped to [64, 1024]; the result is
+ * { max_splits = clamp(ceil(max(1, max_len) / T), 1, PKV_MAX_SPLITS),
+ *   fixed_splits = 0, split_tokens = T }. PKV_EINVAL (and *out untouched) for
+ * an argument outside the ranges above or a NULL out. */
+pkv_status pkv_choose_split(int32_t max_len, int32_t batch, int64_t total_len, int32_t n_kv_heads,
+                            int32_t n_cu, pkv_split_cfg* out);
+
 /* ---- library info ------------------------------------------------------ */
 int pkv_abi_version(void);
 const char* pkv_status_str(pkv_status s);
@@ -204,6 +225,11 @@ pkv_status pkv_build_metadata(const pkv_batch_meta* meta, int32_t mode, pkv_spli
                               int32_t* splits_out, hipStream_t stream);
 
 /* ---- decode workspace ----------------------------------------------------
+ * The split partials live in a caller-owned workspace that is sized once and
+ * passed down to the kernels on every call (P1, bullets on InferenceWorkspace
+ * owning decode_o_part / decode_ml_part, on the C++ kernels taking
+ * pre-allocated buffers, and on allocating once at executor start with no
+ * allocation in the decode loop). This call returns the size.
  * Bytes of workspace one decode call over `batch` requests needs. Layout
  * (offsets from the workspace start, which must be 256-byte aligned):
  *   o_part  fp32 at 0:         [batch, n_q_heads, max_splits, head_dim]
@@ -222,6 +248,10 @@ size_t pkv_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t head
                                   int32_t max_splits);
 
 /* ---- a3 + a4: split-KV paged decode attention ----------------------------
+ * Flash-decoding over the paged cache (P1, bullets on workspace-owned
+ * decode_o_part / decode_ml_part partials that the C++ decode kernels fill,
+ * on reading K/V through the slot table instead of a gathered copy, and on the
+ * B=1 decode latency across 1K-32K contexts).
  * One query token per request: for request b and q head h (KV head h/g),
  *   out[b, h, :] = softmax_j(scale * q[b,h,:] . K[j]) V[j],  j < L_b,
  * with K[j], V[j] read at slot req_to_token[r_b, j] of `layer`. Computed as
@@ -337,6 +367,10 @@ pkv_status pkv_paged_prefill_attn(const pkv_kv_pool* pool, int32_t layer, const 
                                   int32_t causal, void* out, hipStream_t stream);
 
 /* ---- debug validator --------------------------------------------------------
+ * Checks the batch's index arrays before they are trusted (P2, bullets on
+ * validating prefill inputs before KV allocation and on one forward behind a
+ * shared _check_fwd guard; the entry points check their host-visible
+ * arguments the same way, this call extends the check to device contents).
  * Synchronous: copies the metadata to the host (on `stream`, then waits) and
  * checks req_pool_indices in [0, n_req_rows), 0 <= seq_lens <= stride, slots
  * of every live position in [0, n_slots), and for PREFILL qo_indptr

@@ -28,7 +28,8 @@ PKV_MAX_SPLITS = 4096
 
 # Every symbol include/pkv.h declares.
 EXPORTS = (
-    "pkv_abi_version", "pkv_status_str", "pkv_last_error", "pkv_kv_store", "pkv_rope_kv_store",
+    "pkv_abi_version", "pkv_status_str", "pkv_last_error", "pkv_choose_split", "pkv_kv_store",
+    "pkv_rope_kv_store",
     "pkv_build_metadata",
     "pkv_decode_workspace_bytes", "pkv_paged_decode_attn",
     "pkv_decode_step", "pkv_cascade_decode_attn", "pkv_decode_partials",
@@ -84,6 +85,7 @@ def load(path: str = LIB_PATH):
         "pkv_abi_version": (C.c_int, []),
         "pkv_status_str": (C.c_char_p, [I32]),
         "pkv_last_error": (C.c_char_p, []),
+        "pkv_choose_split": (I32, [I32, I32, I64, I32, I32, C.POINTER(SplitCfg)]),
         "pkv_kv_store": (I32, [pool_p, I32, P, P, P, I64, P]),
         "pkv_rope_kv_store": (I32, [pool_p, I32, P, P, I32, P, P, P, P, I32, I32, P, I64, P]),
         "pkv_build_metadata": (I32, [meta_p, I32, SplitCfg, P, P, I64, P, P]),

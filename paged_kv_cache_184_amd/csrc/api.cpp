@@ -203,6 +203,35 @@ const char* pkv_status_str(pkv_status s) {
 
 const char* pkv_last_error(void) { return g_err.c_str(); }
 
+pkv_status pkv_choose_split(int32_t max_len, int32_t batch, int64_t total_len, int32_t n_kv_heads,
+                            int32_t n_cu, pkv_split_cfg* out) {
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  if (max_len < 0 || batch < 1 || n_kv_heads < 1 || n_cu < 1)
+    return fail(PKV_EINVAL, "need max_len >= 0, batch, n_kv_heads, n_cu >= 1 (got %d, %d, %d, %d)",
+                max_len, batch, n_kv_heads, n_cu);
+  const int64_t len = max_len > 0 ? max_len : 1;
+  int64_t tokens;
+  if (batch > 1 && total_len >= 0) {
+    // about two workgroups per CU over all (request, KV head, split) items
+    const int64_t tot = total_len > 0 ? total_len : 1;
+    tokens = (tot * n_kv_heads + 2 * (int64_t)n_cu - 1) / (2 * (int64_t)n_cu);
+  } else {
+    // the longest request's workgroups cover the device about once
+    int64_t want = (int64_t)n_cu / ((int64_t)batch * n_kv_heads);
+    if (want < 1) want = 1;
+    tokens = (len + want - 1) / want;
+  }
+  tokens = (tokens + PKV_SPLIT_ALIGN - 1) / PKV_SPLIT_ALIGN * PKV_SPLIT_ALIGN;
+  tokens = tokens < 64 ? 64 : (tokens > 1024 ? 1024 : tokens);
+  int64_t splits = (len + tokens - 1) / tokens;
+  splits = splits < 1 ? 1 : (splits > PKV_MAX_SPLITS ? PKV_MAX_SPLITS : splits);
+  out->max_splits = (int32_t)splits;
+  out->fixed_splits = 0;
+  out->split_tokens = (int32_t)tokens;
+  out->reserved = 0;
+  return ok();
+}
+
 pkv_status pkv_kv_store(const pkv_kv_pool* pool, int32_t layer, const void* k_new,
                         const void* v_new, const int32_t* loc, int64_t n_tokens,
                         hipStream_t stream) {

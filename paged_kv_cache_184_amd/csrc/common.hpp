@@ -177,6 +177,25 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Merge placement: the q head that merge workgroup x (of n_q_heads) serves.
+// Workgroups reach the 8 XCDs round-robin by linear id, and with n_kv_heads a
+// multiple of 8 the partial kernel (KV head fastest in its grid) writes every
+// split of KV head k from XCD k mod 8. Workgroup x takes a head of KV head
+// (x mod 8) + 8 * (j / g), j = x / 8, so its partials are read on the XCD that
+// wrote them; the map is a bijection of [0, n_q_heads) for every such
+// n_kv_heads and g = n_q_heads / n_kv_heads >= 1. Any other head count
+// (n_kv_heads = 0 included: the merge-only entry point does not know it) keeps
+// the identity.
+__host__ __device__ __forceinline__ int merge_head_of(int x, int n_q_heads, int n_kv_heads) {
+  if (n_kv_heads > 0 && (n_kv_heads & 7) == 0 && n_q_heads >= n_kv_heads &&
+      n_q_heads % n_kv_heads == 0) {
+    const int g = n_q_heads / n_kv_heads;
+    const int j = x >> 3;
+    return ((x & 7) + 8 * (j / g)) * g + j % g;
+  }
+  return x;
+}
+
 // Split rule of pkv_split_cfg: returns S (0 when L <= 0) and the chunk length.
 __host__ __device__ __forceinline__ int split_count(int L, int max_splits, int fixed_splits,
                                                     int split_tokens, int* chunk_out) {

@@ -661,20 +661,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   __shared__ float wts[U];
   const int lane = threadIdx.x;
   const int b = blockIdx.y;
-  // With Hkv a multiple of the 8 XCDs, the partial kernel wrote all splits of
-  // KV head k from XCD k mod 8. Workgroups reach the XCDs round-robin by
-  // linear id (here x mod 8, as Hq is then a multiple of 8 too), so q head h
-  // is taken by an x with x mod 8 = (h / g) mod 8: its partials are read on
-  // the XCD that wrote them. The map is a bijection of [0, Hq) for any such
-  // Hkv and g = Hq / Hkv. Callers that give no KV-head count (the merge-only
-  // entry point leaves it 0) keep h = x.
-  int h = blockIdx.x;
-  const int hkv = a.n_kv_heads;
-  if (hkv > 0 && (hkv & 7) == 0 && a.n_q_heads % hkv == 0) {
-    const int g = a.n_q_heads / hkv;
-    const int j = h >> 3;
-    h = ((h & 7) + 8 * (j / g)) * g + j % g;
-  }
+  // q head of this workgroup: on the XCD that wrote its partials when the
+  // KV-head count allows (a bijection of [0, Hq)); bounded before any index
+  const int h = merge_head_of(blockIdx.x, a.n_q_heads, a.n_kv_heads);
+  if (h < 0 || h >= a.n_q_heads) return;
   const int64_t part = ((int64_t)b * a.n_q_heads + h) * a.split.max_splits;
   const float2* ml = (const float2*)(a.ml_part + 2 * part);
   const float* o = a.o_part + part * D + lane * PER;

@@ -511,9 +511,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // 2^kTau, so that row's sum (of the same rounded weights) exceeds 2^kTau or
   // is not finite. Such a tile is done again: one pass gathers the exact row
   // maxima, the last one uses them as the stabiliser and cannot overflow.
+  // Tested on the bits, so that NaN (an inf weight minus an inf) is caught
+  // whatever the file's floating-point flags let the compiler assume.
   bool bad = false;
 #pragma unroll
-  for (int n = 0; n < 2; ++n) bad |= !(lacc[n][0] <= kSumLimit);
+  for (int n = 0; n < 2; ++n)
+    bad |= (__float_as_uint(lacc[n][0]) & 0x7fffffffu) > __float_as_uint(kSumLimit);
   // workgroup-wide decision; the barrier also frees the stages for the next pass
   if (lane == 0) redo[wave] = __builtin_amdgcn_ballot_w64(bad) != 0;
   __syncthreads();

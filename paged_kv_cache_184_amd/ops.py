@@ -114,21 +114,14 @@ def split_cfg(max_splits: int, fixed_splits: int = 0, split_tokens: int = 256) -
 
 def choose_split(max_len: int, batch: int, n_kv_heads: int, n_cu: int = 256,
                  total_len: Optional[int] = None) -> SplitCfg:
-    """A host-side split choice, 64..1024 tokens per split.
-
-    One request: enough splits to cover the GPU about once (one workgroup of
-    4 waves per CU). Several requests with their total length known: about
-    two workgroups per CU over all (request, KV head, split) items, from the
-    total length, so short and long requests share the CUs evenly; without
-    the total, the longest request covers the GPU once."""
-    if batch > 1 and total_len is not None:
-        tokens = -(-max(1, total_len) * n_kv_heads // (2 * n_cu))
-    else:
-        want = max(1, n_cu // max(1, batch * n_kv_heads))
-        tokens = -(-max(1, max_len) // want)
-    tokens = min(1024, max(64, -(-tokens // 16) * 16))
-    max_splits = max(1, min(_lib.PKV_MAX_SPLITS, -(-max(1, max_len) // tokens)))
-    return SplitCfg(max_splits, 0, tokens, 0)
+    """The library's default split configuration for a decode batch
+    (pkv_choose_split; the rule is documented in include/pkv.h). A host-only
+    call: no GPU is needed."""
+    out = SplitCfg()
+    _check(lib().pkv_choose_split(int(max_len), int(batch),
+                                  -1 if total_len is None else int(total_len), int(n_kv_heads),
+                                  int(n_cu), C.byref(out)))
+    return out
 
 
 # ----------------------------------------------------------------- entry points
