@@ -7,7 +7,9 @@
  * the work is enqueued on `stream` and the call returns without synchronising;
  * the library never allocates device memory, never reads device data on the
  * host (except pkv_validate_meta, a debug aid) and keeps no pointer after it
- * returns, so the calls may be captured into a HIP graph.
+ * returns, so the calls may be captured into a HIP graph. The one piece of
+ * device state it holds is the fixed scratch array of
+ * pkv_paged_decode_attn_noalloc, part of the code object, one per device.
  *
  * Citation key for the pages this library follows (AstrAI commit pages; a
  * "bullet" is one line of the commit message shown on that page):
@@ -284,6 +286,27 @@ pkv_status pkv_decode_step(const pkv_kv_pool* pool, int32_t layer, const void* q
                            const pkv_batch_meta* meta, float scale, pkv_split_cfg split,
                            int32_t* kv_indptr_out, int32_t* loc_out, int32_t* splits_out,
                            void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+
+/* ---- decode without a caller workspace -----------------------------------
+ * For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * result of pkv_paged_decode_attn with the same arguments, computed by the
+ * same kernels, with the split partials in a scratch array the library holds
+ * in each device's memory (PKV_NOALLOC_SCRATCH_BYTES, kept until the process
+ * ends) instead of a caller workspace. The call allocates nothing; its first
+ * call on a device looks up that device's scratch address (with the device
+ * current), later calls reuse it. Needs
+ * pkv_decode_workspace_bytes(batch, n_q_heads, head_dim, split.max_splits)
+ * <= PKV_NOALLOC_SCRATCH_BYTES, else PKV_EWORKSPACE before anything is
+ * enqueued. Every call on a device shares that device's scratch, which keeps
+ * the last call's partials (no call needs it cleared): calls that overlap in
+ * time on one device (other streams, other threads) race and must not be
+ * issued; the caller serialises them. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+pkv_status pkv_paged_decode_attn_noalloc(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                         int32_t n_q_heads, const pkv_batch_meta* meta,
+                                         float scale, pkv_split_cfg split, void* out,
+                                         hipStream_t stream);
 
 /* ---- cascade (shared-prefix) decode --------------------------------------
  * Requests of a prefix group map their first P positions to the same slots

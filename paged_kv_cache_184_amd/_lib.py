@@ -25,13 +25,14 @@ PKV_MODE_DECODE = 0
 PKV_MODE_PREFILL = 1
 PKV_SPLIT_ALIGN = 16
 PKV_MAX_SPLITS = 4096
+PKV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/pkv.h declares.
 EXPORTS = (
     "pkv_abi_version", "pkv_status_str", "pkv_last_error", "pkv_choose_split", "pkv_kv_store",
     "pkv_rope_kv_store",
     "pkv_build_metadata",
-    "pkv_decode_workspace_bytes", "pkv_paged_decode_attn",
+    "pkv_decode_workspace_bytes", "pkv_paged_decode_attn", "pkv_paged_decode_attn_noalloc",
     "pkv_decode_step", "pkv_cascade_decode_attn", "pkv_decode_partials",
     "pkv_decode_merge", "pkv_paged_prefill_attn", "pkv_validate_meta",
 )
@@ -93,6 +94,7 @@ def load(path: str = LIB_PATH):
         "pkv_decode_step": (I32, [pool_p, I32, P, P, P, I32, meta_p, F32, SplitCfg, P, P, P, P, SZ,
                                   P, P]),
         "pkv_paged_decode_attn": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P, P]),
+        "pkv_paged_decode_attn_noalloc": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, P]),
         "pkv_cascade_decode_attn": (I32, [pool_p, I32, P, I32, meta_p, groups_p, F32, SplitCfg, P,
                                           SZ, P, P]),
         "pkv_decode_partials": (I32, [pool_p, I32, P, I32, meta_p, F32, SplitCfg, P, SZ, P]),

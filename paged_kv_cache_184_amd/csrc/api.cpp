@@ -389,6 +389,39 @@ pkv_status pkv_paged_decode_attn(const pkv_kv_pool* pool, int32_t layer, const v
   return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
 }
 
+pkv_status pkv_paged_decode_attn_noalloc(const pkv_kv_pool* pool, int32_t layer, const void* q,
+                                         int32_t n_q_heads, const pkv_batch_meta* meta,
+                                         float scale, pkv_split_cfg split, void* out,
+                                         hipStream_t stream) {
+  // the arguments and the scratch size first: nothing touches the device on error
+  pkv_status s;
+  if ((s = check_pool(pool, layer)) != PKV_OK) return s;
+  if ((s = check_heads(pool, n_q_heads)) != PKV_OK) return s;
+  if ((s = check_meta(meta, false)) != PKV_OK) return s;
+  if ((s = check_split(split)) != PKV_OK) return s;
+  if (meta->batch == 0) return ok();
+  const size_t need = ws_bytes_for(meta->batch, n_q_heads, pool->head_dim, split.max_splits, nullptr);
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_EWORKSPACE,
+                "the partials need %zu bytes, above the %zu-byte scratch of the no-allocation call "
+                "(use pkv_paged_decode_attn with a workspace)",
+                need, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+  if (!out) return fail(PKV_EINVAL, "out is NULL");
+  if (!aligned16(out)) return fail(PKV_EALIGN, "out must be 16-byte aligned");
+  void* scratch = nullptr;
+  hipError_t e = pkv::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_status(e, "no-allocation scratch lookup");
+  pkv::DecodeArgs a{};
+  s = decode_prepare(pool, layer, q, n_q_heads, meta, scale, split, scratch,
+                     (size_t)PKV_NOALLOC_SCRATCH_BYTES, &a);
+  if (s != PKV_OK) return s;
+  a.out = out;
+  a.merge_multi_only = true;
+  e = pkv::launch_decode_partials(a, stream);
+  if (e != hipSuccess) return hip_status(e, "decode partial launch");
+  return hip_status(pkv::launch_decode_merge(a, stream), "decode merge launch");
+}
+
 pkv_status pkv_cascade_decode_attn(const pkv_kv_pool* pool, int32_t layer, const void* q,
                                    int32_t n_q_heads, const pkv_batch_meta* meta,
                                    const pkv_prefix_groups* groups, float scale,

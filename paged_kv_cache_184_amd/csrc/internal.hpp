@@ -60,6 +60,9 @@ hipError_t launch_cascade_partials(const DecodeArgs& a, hipStream_t stream);
 int cascade_tiles(int n_q_heads, int n_kv_heads, int max_members);
 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
+// Device address of the current device's no-allocation scratch
+// (PKV_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up on first use.
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 

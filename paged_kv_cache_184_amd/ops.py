@@ -234,6 +234,21 @@ def paged_decode_attn(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: flo
     return out
 
 
+def paged_decode_attn_noalloc(q, k_pool, v_pool, layer: int, meta: BatchMeta, scale: float,
+                              split: SplitCfg, out, stream=None, kv_scales=None):
+    """Split-KV paged decode with the partials in the library's own device
+    scratch (pkv_paged_decode_attn_noalloc): no workspace, no allocation; ``out``
+    must be given. Calls on one device must not overlap in time."""
+    pool = make_pool(k_pool, v_pool, kv_scales)
+    _q_check(q, pool, meta.batch)
+    _need(out is not None and out.is_contiguous() and out.shape == q.shape and
+          out.dtype == q.dtype, "out")
+    _check(lib().pkv_paged_decode_attn_noalloc(C.byref(pool), layer, q.data_ptr(), q.shape[1],
+                                               C.byref(meta), scale, split, out.data_ptr(),
+                                               _stream(stream)))
+    return out
+
+
 def make_prefix_groups(prefix_len: torch.Tensor, group_indptr: torch.Tensor,
                        members: torch.Tensor, max_members: int) -> _lib.PrefixGroups:
     """Descriptor of the shared-prefix groups of a batch (device int32 tensors)."""

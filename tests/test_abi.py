@@ -313,3 +313,29 @@ def test_decode_step_rejects(lib):
 def test_validate_meta_rejects(lib):
     assert lib.pkv_validate_meta(C.byref(_meta()), 3, 10, 0, None) == _lib.PKV_EINVAL
     assert lib.pkv_validate_meta(None, 0, 10, 0, None) == _lib.PKV_EINVAL
+
+
+def test_noalloc_decode_rejects_before_any_device_work(lib):
+    """pkv_paged_decode_attn_noalloc checks its arguments and the scratch size
+    before it looks up the scratch or enqueues anything (runs without a GPU)."""
+    f = lib.pkv_paged_decode_attn_noalloc
+    meta = _meta()
+    # 1 request x 4 q heads x 4096 splits x 64 x 4 bytes = 4 MiB: fits
+    assert lib.pkv_decode_workspace_bytes(1, 4, 64, 4096) <= _lib.PKV_NOALLOC_SCRATCH_BYTES
+    # 64 requests x 32 q heads x 64 splits x 128 x 4 bytes = 64 MiB: too large
+    big_pool = _pool(n_kv_heads=8, head_dim=128)
+    big_meta = _meta(batch=64)
+    assert f(C.byref(big_pool), 0, 16, 32, C.byref(big_meta), 0.125, _split(max_splits=64), 16,
+             None) == _lib.PKV_EWORKSPACE
+    assert b"scratch" in lib.pkv_last_error()
+    assert f(None, 0, 16, 4, C.byref(meta), 0.125, _split(), 16, None) == _lib.PKV_EINVAL
+    assert f(C.byref(_pool()), 0, 16, 3, C.byref(meta), 0.125, _split(), 16, None) == _lib.PKV_ESHAPE
+    assert f(C.byref(_pool()), 0, 16, 4, C.byref(meta), 0.125, _split(max_splits=0), 16,
+             None) == _lib.PKV_EINVAL
+    assert f(C.byref(_pool()), 0, 16, 4, C.byref(meta), 0.125, _split(), None,
+             None) == _lib.PKV_EINVAL
+    assert f(C.byref(_pool()), 0, 16, 4, C.byref(meta), 0.125, _split(), 24,
+             None) == _lib.PKV_EALIGN
+    # an empty batch is a successful no-op
+    assert f(C.byref(_pool()), 0, None, 4, C.byref(_meta(batch=0)), 0.125, _split(), None,
+             None) == _lib.PKV_OK
