@@ -377,7 +377,7 @@ pkv_status pkv_decode_merge(const pkv_batch_meta* meta, int32_t n_q_heads, int32
  * start into one forward; P1, bullet on cached prefix pages). The new tokens'
  * K/V must already be stored (pkv_kv_store). q, out: device
  * [total_q, n_q_heads, head_dim], 16-byte aligned. max_q_len >= every n_b sizes
- * the grid (rows i >= max_q_len are not computed). BF16 or FP8_E4M3 pools
+ * the launch; rows i >= max_q_len of a request are never written. BF16 or FP8_E4M3 pools
  * (F32 returns PKV_EUNSUPPORTED; for FP8_E4M3, q and out are BF16 and the
  * codes are widened exactly to bf16, the K scale joining the softmax scale and
  * the V scale the output): QK^T and PV run on bf16 MFMA with fp32

@@ -37,9 +37,12 @@
 //     those lanes at keys base+4g+0..3 and columns 16dt+4(s%4) gives every
 //     lane the 4 keys it needs at its own column.
 // Only blocks that straddle the causal diagonal or the sequence end are
-// masked. Tiles are issued longest-first (highest token offset first).
+// masked. Up to 64 requests, the (request, tile) items run in decreasing cost
+// over the whole batch (a 1-D launch, KV head fastest); larger batches use a
+// (tile, KV head, request) grid, each request's longest tiles first.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -277,6 +280,81 @@ __device__ __forceinline__ void attend_block(
   }
 }
 
+// Largest batch whose tiles are ordered by cost (one request per lane of a wave).
+constexpr int kSortedMaxBatch = 64;
+
+// Work item k of the sorted launch order (batch <= kSortedMaxBatch): items are
+// the (request, query tile) pairs in decreasing cost, the cost of a tile being
+// the 64-key blocks it reads (ties in request order, then decreasing tile), and
+// the KV head is fastest, so the heads of one item run side by side and, with
+// the KV head count a multiple of 8, each XCD serves one head of every request.
+// Greedy dispatch of the longest tiles first leaves only short ones for the
+// end of the launch. Every wave computes the same answer from the request
+// words (one request per lane): the cost c of item k is the largest c with
+// more than k tiles of cost >= c, found by bisection on counts that are closed
+// forms per request. Returns false when k is past the last item.
+template <int BQ>
+__device__ bool sorted_item(const PrefillArgs& a, int k, int& b, int& kvh, int& tile) {
+  const int lane = threadIdx.x & 63;
+  const int item = k / a.n_kv_heads;
+  kvh = k - item * a.n_kv_heads;
+  // this lane's request, clamped as the tile code clamps it
+  int n = 0, P = 0, nt = 0, cmax = 0;
+  if (lane < a.batch) {
+    const int q0 = a.qo_indptr[lane];
+    const int q1 = a.qo_indptr[lane + 1];
+    int L = a.seq_lens[lane];
+    L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
+    n = q1 - q0;
+    n = n < 0 ? 0 : (n > L ? L : n);
+    P = L - n;
+    nt = min((n + BQ - 1) / BQ, (a.max_q_len + BQ - 1) / BQ);
+    if (nt > 0) {
+      const int last_end = a.causal ? P + min(nt * BQ, n) : L;
+      cmax = (last_end + kBK - 1) / kBK;
+    }
+  }
+  // tiles of this lane's request that read at least c blocks
+  auto count = [&](int c) -> int {
+    if (nt == 0) return 0;
+    if (!a.causal) return cmax >= c ? nt : 0;
+    const int64_t thr = (int64_t)kBK * (c - 1) - P;  // tile t reads >= c blocks iff its
+    if (thr < 0) return nt;                           // last key P + min((t+1) BQ, n) - 1
+    if (n <= thr) return 0;                           // is at least thr
+    return max(0, nt - (int)(thr / BQ));
+  };
+  auto wave_add = [](int x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+  };
+  int hi = cmax;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) hi = max(hi, __shfl_xor(hi, off));
+  if (item >= wave_add(nt)) return false;
+  // count(lo) > item >= count(hi)
+  int lo = 1;
+  hi += 1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (wave_add(count(mid)) > item) lo = mid; else hi = mid;
+  }
+  const int above = count(lo + 1);            // this request's tiles costlier than lo
+  const int m = count(lo) - above;            // its tiles of cost exactly lo
+  int o = item - wave_add(above);             // rank among the tiles of cost lo
+  b = 0;
+  for (int i = 0; i < a.batch; ++i) {         // uniform walk over the requests
+    const int mi = __shfl(m, i);
+    if (o < mi) {
+      b = i;
+      tile = __shfl(nt - above, i) - 1 - o;   // decreasing tile index within the cost
+      return true;
+    }
+    o -= mi;
+  }
+  return false;  // not reached: the counts cover item
+}
+
 template <int D, int G, typename KV>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Gm = PGeo<D>;
@@ -298,9 +376,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // wave-uniform: the LDS destinations of the transfers (M0) are then
   // computed in scalar registers, not read back from a vector lane per transfer
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int tile = gridDim.x - 1 - blockIdx.x;  // longest work first
+  int kvh, b, tile;
+  if (a.sorted) {
+    if (!sorted_item<BQ>(a, blockIdx.x, b, kvh, tile)) return;
+    b = __builtin_amdgcn_readfirstlane(b);
+    kvh = __builtin_amdgcn_readfirstlane(kvh);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+  } else {
+    kvh = blockIdx.y;
+    b = blockIdx.z;
+    tile = gridDim.x - 1 - blockIdx.x;  // longest work of the request first
+  }
   const int t0 = tile * BQ;
 
   // the request's words as scalar loads, all in flight before any is used
@@ -534,7 +620,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int rr = wave * 32 + n * 16 + col;
-    if (tok[n] >= n_new) continue;
+    if (tok[n] >= n_new || tok[n] >= a.max_q_len) continue;  // rows past max_q_len stay unwritten
     const int64_t orow = ((int64_t)q0 + tok[n]) * a.n_q_heads + (int64_t)kvh * G + rr % G;
     const int64_t t_abs = (int64_t)q0 + tok[n];
     if (t_abs < 0 || t_abs >= a.total_q) continue;
@@ -554,10 +640,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
 }
 
 template <int D, typename KV>
-hipError_t prefill_for_dim(const PrefillArgs& a, hipStream_t stream) {
+hipError_t prefill_for_dim(PrefillArgs a, hipStream_t stream) {
   const int g = a.n_q_heads / a.n_kv_heads;
   const int bq = kRows / g;
-  dim3 grid((a.max_q_len + bq - 1) / bq, a.n_kv_heads, a.batch);
+  const int64_t tiles_max = (a.max_q_len + bq - 1) / bq;
+  dim3 grid((unsigned)tiles_max, a.n_kv_heads, a.batch);
+  a.sorted = 0;
+  if (a.batch <= kSortedMaxBatch) {
+    // every (request, tile) item once: at most ceil(total_q / BQ) + batch items
+    const int64_t items = std::min<int64_t>(tiles_max * a.batch,
+                                            ((int64_t)a.total_q + bq - 1) / bq + a.batch);
+    const int64_t blocks = items * a.n_kv_heads;
+    if (blocks <= 0x7fffffff / kThreads) {
+      a.sorted = 1;
+      grid = dim3((unsigned)blocks, 1, 1);
+    }
+  }
   switch (g) {
     case 1: prefill_kernel<D, 1, KV><<<grid, kThreads, 0, stream>>>(a); break;
     case 2: prefill_kernel<D, 2, KV><<<grid, kThreads, 0, stream>>>(a); break;

@@ -199,3 +199,51 @@ def test_poisoned_pool_stays_finite():
                  dtype="bf16", seq_lens=[77, 129, 3], n_new=[77, 60, 2], seed=270)
     db, out = check_batch(b, 271)
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("n_req,causal", [(64, True), (64, False), (70, True)])
+def test_many_requests_every_row(n_req, causal):
+    """Up to 64 requests the tiles run in decreasing cost over the whole batch
+    (a 1-D launch whose work items are found per workgroup); above 64 in the
+    per-request grid. Lengths mix empty requests, one-token requests, tails
+    around the tile and the 64-key block, and prefixes: every row must be
+    computed exactly once and match the oracle."""
+    rng = np.random.default_rng(280 + n_req)
+    n_new = rng.integers(0, 90, n_req)
+    n_new[::9] = 0
+    n_new[1::11] = 1
+    prefix = rng.integers(0, 300, n_req)
+    prefix[::5] = 0
+    b = W.custom(f"many{n_req}", n_layers=1, n_slots=1 << 15, n_q_heads=8, n_kv_heads=2,
+                 head_dim=64, dtype="bf16", seq_lens=prefix + n_new, n_new=n_new,
+                 seed=281 + n_req)
+    check_batch(b, 282 + n_req, causal=causal)
+
+
+@pytest.mark.parametrize("n_req", [5, 70])
+def test_rows_past_max_q_len_not_computed(n_req):
+    """max_q_len below some request's new-token count: rows i >= max_q_len are
+    left untouched (the NaN fill stays), every other row matches the oracle."""
+    rng = np.random.default_rng(290 + n_req)
+    n_new = rng.integers(1, 120, n_req)
+    n_new[0] = 119
+    prefix = rng.integers(0, 200, n_req)
+    b = W.custom(f"maxq{n_req}", n_layers=1, n_slots=1 << 15, n_q_heads=8, n_kv_heads=2,
+                 head_dim=128, dtype="bf16", seq_lens=prefix + n_new, n_new=n_new,
+                 seed=291 + n_req)
+    vals = W.host_values(b, 292 + n_req)
+    db = DeviceBatch(b, vals)
+    store_prefill_tokens(db, 0)
+    max_q = 50
+    out = torch.full_like(db.q, float("nan"))
+    ops.paged_prefill_attn(db.q, db.k_pool, db.v_pool, 0, db.meta(with_qo=True), max_q,
+                           b.scale, True, out=out)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    kept = [t for i in range(b.batch)
+            for t in range(int(b.qo_indptr[i]), int(b.qo_indptr[i + 1]))
+            if t - int(b.qo_indptr[i]) < max_q]
+    skipped = sorted(set(range(b.total_q)) - set(kept))
+    assert skipped and np.all(np.isnan(out[skipped]))
+    ref = oracle_prefill(b, vals, 0, rows=kept)
+    compare(out[kept], ref[kept], "bf16", f"{n_req} requests, max_q_len {max_q}")
