@@ -319,32 +319,6 @@ class DecodeBench:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * n_per_graph)
 
-    def check(self) -> float:
-        """Max abs error of the last output against the oracle (layer 0 state)."""
-        import oracle as O
-
-        b = self.b
-        layer = 0
-        self.step(0)
-        self.torch.cuda.synchronize()
-        L = int(b.seq_lens[0])
-        slots = b.req_to_token[b.req_pool_indices[0], :L]
-        idx = self.torch.from_numpy(slots.astype(np.int64)).to("cuda")
-        r2t = np.arange(L, dtype=np.int32)[None]
-        q = self.q[:1].float().cpu().numpy()
-        if self.kv == "fp8":
-            k = self.k_pool[layer].index_select(0, idx).cpu().numpy()[None]
-            v = self.v_pool[layer].index_select(0, idx).cpu().numpy()[None]
-            ref = O.decode_attention_fp8(q, k, v, self.kv_scales.cpu().numpy(), 0, r2t,
-                                         np.array([0], np.int32), np.array([L], np.int32),
-                                         b.scale)
-        else:
-            k = self.k_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
-            v = self.v_pool[layer].index_select(0, idx).float().cpu().numpy()[None]
-            ref = O.decode_attention(q, k, v, 0, r2t, np.array([0], np.int32),
-                                     np.array([L], np.int32), b.scale)
-        return float(np.abs(self.out[:1].float().cpu().numpy() - ref).max())
-
     def oracle_inputs(self):
         b = self.b
         L = int(b.seq_lens[0])
@@ -354,6 +328,13 @@ class DecodeBench:
         v = self.v_pool[0].index_select(0, idx).float().cpu().numpy()[None]
         return (self.q[:1].float().cpu().numpy(), k, v, np.arange(L, dtype=np.int32)[None],
                 np.array([0], np.int32), np.array([L], np.int32), b.scale)
+
+
+def spread_us(ms_sorted):
+    """[p10, p50, p90] in microseconds of sorted per-launch times in ms."""
+    n = len(ms_sorted)
+    pick = lambda q: ms_sorted[min(n - 1, int(q * (n - 1) + 0.5))] * 1e3
+    return [round(pick(0.1), 1), round(pick(0.5), 1), round(pick(0.9), 1)]
 
 
 def _time_calls(fn, steps: int) -> float:
@@ -490,8 +471,12 @@ class PrefillBench:
         return float(4 * b.head_dim * b.n_q_heads * np.sum(n * P + n * (n + 1) / 2))
 
     def run(self, steps: int, warmup: int):
+        """(ms per step, mean ms per prefill launch, the launches' ms sorted).
+        The warm-up runs at least 64 steps: the core clock climbs for tens of
+        milliseconds of sustained MFMA work, and a launch right after a short
+        warm-up runs up to 20% slower than in steady state."""
         torch = self.torch
-        for i in range(warmup):
+        for i in range(max(warmup, 64)):
             for c in self.calls[i % len(self.calls)]:
                 c()
         torch.cuda.synchronize()
@@ -510,8 +495,8 @@ class PrefillBench:
         end.record()
         torch.cuda.synchronize()
         step_ms = start.elapsed_time(end) / steps
-        attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        return step_ms, attn_ms
+        each = sorted(a.elapsed_time(b) for a, b in evs)
+        return step_ms, float(np.mean(each)), each
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_b1_32k_traffic.json")
@@ -554,11 +539,18 @@ def cpu_baseline(db: DecodeBench, seconds: float):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    import torch
+
     args = db.oracle_inputs()
+    # the GPU's output for layer 0 of the same workload, checked against the
+    # oracle's result from the timed calls below
+    db.step(0)
+    torch.cuda.synchronize()
+    got = db.out[:1].float().cpu().numpy()
     reps = 0
     t0 = time.perf_counter()
     while True:
-        O.decode_attention(args[0], args[1], args[2], 0, args[3], args[4], args[5], args[6])
+        ref = O.decode_attention(args[0], args[1], args[2], 0, args[3], args[4], args[5], args[6])
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -571,6 +563,7 @@ def cpu_baseline(db: DecodeBench, seconds: float):
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "host_cpu_count": os.cpu_count(), "host_cpus_usable": affinity,
             "blas_threads": int(threads),
+            "gpu_vs_oracle_max_abs_err": float(np.abs(got - ref).max()),
             "sample": f"{reps} full oracle decode calls (B=1, ctx {db.b.seq_lens[0]}, 32 q heads) "
                       f"in {el:.1f} s; cores = BLAS threads (threadpoolctl), the only "
                       f"multi-threaded part of the oracle"}
@@ -599,7 +592,6 @@ def main():
         db.mode = "fused"
         step_ms, host_s = db.run(args.steps, args.warmup)
         part_ms = db.run_partials(args.steps, args.warmup)
-        err = db.check()
         entry = {
             "us_per_step": round(step_ms * 1e3, 2),
             "kv_gbs": round(db.kv_bytes() / (step_ms * 1e-3) / 1e9, 1),
@@ -609,13 +601,15 @@ def main():
             "separate_calls_us_per_step": round(sep_ms * 1e3, 2),
             "splits": int(db.split.max_splits),
             "split_tokens": int(db.split.split_tokens),
-            "max_abs_err": err,
         }
         if args.graph or ctx == args.headline:
             g_ms = db.run_graph(args.steps)
             entry["graph_us_per_step"] = round(g_ms * 1e3, 2)
             entry["graph_kv_gbs"] = round(db.kv_bytes() / (g_ms * 1e-3) / 1e9, 1)
         if ctx == args.headline:
+            # spread: ten more timed regions of the same length, each between two events
+            reps = sorted(db.run(args.steps, 2)[0] for _ in range(10))
+            entry["us_per_step_repeats_p10_p50_p90"] = spread_us(reps)
             # the same step repeated on one layer: its K/V stay in the 256 MB
             # Infinity Cache between steps (labelled warm; not the headline)
             w_ms = db.run_warm_same_layer(args.steps, args.warmup)
@@ -644,7 +638,6 @@ def main():
             "partial_kernel_gbs": round(db8.partial_kernel_bytes() / (part8 * 1e-3) / 1e9, 1),
             "step_speedup_vs_bf16": round(head[1] / step8, 3),
             "splits": int(db8.split.max_splits), "split_tokens": int(db8.split.split_tokens),
-            "max_abs_err": db8.check(),
         }
         detail[f"{ctx // 1024}k_fp8"] = entry
         print(f"# ctx {ctx} fp8: {entry}", file=sys.stderr, flush=True)
@@ -667,7 +660,6 @@ def main():
             steps = max(10, args.steps // 4)
             db.mode = "fused"
             step_ms, _ = db.run(steps, max(2, args.warmup // 4))
-            err = db.check()
             b = db.b
             detail[name] = {
                 "batch": b.batch, "n_q_heads": b.n_q_heads, "sum_seq_lens": int(b.seq_lens.sum()),
@@ -677,8 +669,7 @@ def main():
                 "pct_hbm_peak_unique": round(100 * (db.step_bytes() - db.kv_bytes() +
                                                     db.kv_bytes_unique()) /
                                              (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
-                "splits": int(db.split.max_splits), "split_tokens": int(db.split.split_tokens),
-                "max_abs_err_request0": err}
+                "splits": int(db.split.max_splits), "split_tokens": int(db.split.split_tokens)}
             if db.cascade is not None:
                 # attention alone: plain decode vs cascade (the shared prefix read
                 # once per group); the split cap leaves room for prefix splits
@@ -698,11 +689,12 @@ def main():
         detail["new_token_steps"] = new_token_steps(max(20, args.steps // 4))
         print(f"# new-token steps: {detail['new_token_steps']}", file=sys.stderr, flush=True)
         pb = PrefillBench(n_layers=8, seed=184_004)
-        p_step, p_attn = pb.run(max(10, args.steps // 5), 3)
+        p_step, p_attn, p_each = pb.run(max(20, args.steps // 5), args.warmup)
         tflops = pb.flops() / (p_attn * 1e-3) / 1e12
         detail["prefill"] = {
             "workload": "packed_prefill (8 requests, T_q=%d)" % pb.b.total_q,
             "us_per_step": round(p_step * 1e3, 1), "kernel_us": round(p_attn * 1e3, 1),
+            "kernel_us_p10_p50_p90": spread_us(p_each),
             "gflop": round(pb.flops() / 1e9, 1), "tflops": round(tflops, 1),
             "mfma_util_pct": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 1)}
         print(f"# prefill: {detail['prefill']}", file=sys.stderr, flush=True)
@@ -710,10 +702,11 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_fp8:
             pb = PrefillBench(n_layers=8, seed=184_024, kv="fp8")
-            p8_step, p8_attn = pb.run(max(10, args.steps // 5), 3)
+            p8_step, p8_attn, p8_each = pb.run(max(20, args.steps // 5), args.warmup)
             detail["prefill_fp8"] = {
                 "workload": "packed_prefill (8 requests, T_q=%d), E4M3 pools" % pb.b.total_q,
                 "us_per_step": round(p8_step * 1e3, 1), "kernel_us": round(p8_attn * 1e3, 1),
+                "kernel_us_p10_p50_p90": spread_us(p8_each),
                 "tflops": round(pb.flops() / (p8_attn * 1e-3) / 1e12, 1),
                 "kernel_vs_bf16": round(p_attn / p8_attn, 3)}
             print(f"# prefill fp8: {detail['prefill_fp8']}", file=sys.stderr, flush=True)

@@ -245,3 +245,57 @@ def test_rope_kv_store_fp8(d, interleaved):
         f"{int((got_v != vc).sum())} V code mismatches")
     assert np.array_equal(got_k, kc) and np.array_equal(got_v, vc)
     compare_rounded(q_out.float().cpu().numpy(), q_ref, "bf16", "rotated q")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("interleaved", [True, False])
+def test_rope_kv_store_fp8_plain_definition(d, interleaved):
+    """The quantising RoPE store against the plain definition, independent of
+    the fp32 operation order R21 fixes: the fp64 rotation, its quotient by the
+    layer's K scale, the nearest E4M3 code. The kernel rotates in fp32 (each
+    product and sum rounded once) and divides in fp32, so its quotient lies
+    within E = 2^-22 (|a c| + |b s| + |a'|) / scale of the fp64 one; a code may
+    differ from the plain one only where an E4M3 rounding boundary lies within
+    E of the fp64 quotient, and then only to the code on the other side of it.
+    Every other K code and every V code must equal the plain definition's."""
+    rng = np.random.default_rng(670 + d + interleaved)
+    T, hkv, n_slots, max_pos = 53, 2, 200, 4096
+    k = (W.normal_values((T, hkv, d), 671, "bf16") * 4).astype(np.float32)  # some saturate
+    v = W.normal_values((T, hkv, d), 672, "bf16")
+    kp = rng.choice(FINITE, size=(1, n_slots, hkv, d)).astype(np.uint8)
+    vp = rng.choice(FINITE, size=(1, n_slots, hkv, d)).astype(np.uint8)
+    pos = rng.integers(0, max_pos, size=T).astype(np.int32)
+    loc = rng.permutation(n_slots)[:T].astype(np.int32)
+    scales = np.float32([[0.03, 0.02]])
+    tab = W.rope_freqs_cis(max_pos, d)
+    kd, vd = to_dev(kp), to_dev(vp)
+    ops.rope_kv_store(kd, vd, 0, to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(pos),
+                      to_dev(tab), to_dev(loc), interleaved=interleaved, kv_scales=to_dev(scales))
+    torch.cuda.synchronize()
+    got_k = kd.cpu().numpy()[0, loc]
+    got_v = vd.cpu().numpy()[0, loc]
+    ks = float(scales[0, 0])
+    k_rot = O.apply_rope(k, pos, tab, interleaved)  # fp64
+    y = k_rot / ks
+    plain = O.e4m3_encode(y)
+    # |a c| + |b s| of every output element: its own input times |cos| plus its
+    # partner's times |sin|, with the table's fp32 values
+    x = np.asarray(k, np.float64)
+    partner = np.empty_like(x)
+    cs = np.empty_like(x)
+    sn = np.empty_like(x)
+    for i, (a, b) in enumerate(O.rope_pairs(d, interleaved)):
+        partner[..., a], partner[..., b] = x[..., b], x[..., a]
+        c = tab[pos, i, 0].astype(np.float64)[:, None]
+        s = tab[pos, i, 1].astype(np.float64)[:, None]
+        cs[..., a], cs[..., b] = c, c
+        sn[..., a], sn[..., b] = s, s
+    E = 2.0 ** -22 * (np.abs(x * cs) + np.abs(partner * sn) + np.abs(k_rot)) / ks
+    lo, hi = O.e4m3_encode(y - E), O.e4m3_encode(y + E)
+    exact = got_k == plain
+    near = (lo != hi) & ((got_k == lo) | (got_k == hi))
+    say(f"  rope fp8 plain d={d} interleaved={interleaved}: {int((~exact).sum())} K codes "
+        f"off the plain definition, all within E of a rounding boundary: "
+        f"{bool(np.all(exact | near))}; {int((lo != hi).sum())} boundary cases")
+    assert np.all(exact | near)
+    assert np.array_equal(got_v, O.quantize(v, float(scales[0, 1])))
