@@ -175,7 +175,7 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Merge placement: the q head that merge workgroup x (of n_q_heads) serves.
 // Workgroups reach the 8 XCDs round-robin by linear id, and with n_kv_heads a

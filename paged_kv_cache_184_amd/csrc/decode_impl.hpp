@@ -501,6 +501,56 @@ __device__ __forceinline__ void finish_split(const DecodeArgs& a, const float* r
   }
 }
 
+// Reduce-scatter of NV values per lane over the 64 / LPR token groups of a
+// wave (lane = LPR grp + c): after it, v[k] of a lane holds the sum over the
+// groups of element first + k of the lanes with its c, for k < NV / groups;
+// returns first. Each halving step moves one half of the live values to the
+// partner group and adds: lane halves (xor 32) and row pairs (xor 16) with the
+// gfx950 row-swap instructions, and, with 8 lanes per row, row halves (xor 8)
+// with a DPP rotation. Which half a lane keeps after a swap is read off the
+// same instruction applied to the half indices, so no lane layout is assumed.
+template <int LPR, int NV>
+__device__ __forceinline__ int group_reduce_scatter(float (&v)[NV], int lane) {
+  static_assert(NV % (64 / LPR) == 0, "values per lane");
+  int first = 0;
+  constexpr int H1 = NV / 2;
+  {
+    const auto t = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);  // 0: kept first half
+    first += (int)t[0] * H1;
+#pragma unroll
+    for (int k = 0; k < H1; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]),
+                                                      __float_as_uint(v[k + H1]), false, false);
+      v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  constexpr int H2 = NV / 4;
+  {
+    const auto t = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
+    first += (int)t[0] * H2;
+#pragma unroll
+    for (int k = 0; k < H2; ++k) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[k]),
+                                                      __float_as_uint(v[k + H2]), false, false);
+      v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (LPR == 8) {
+    // lanes 0-7 of each row keep the first half, lanes 8-15 the second; each
+    // adds the value of the lane 8 away in its row (row_ror:8)
+    constexpr int H3 = NV / 8;
+    const bool hi = (lane & 8) != 0;
+    first += hi ? H3 : 0;
+#pragma unroll
+    for (int k = 0; k < H3; ++k) {
+      const float x = hi ? v[k + H3] : v[k];
+      const float y = hi ? v[k] : v[k + H3];
+      v[k] = x + dpp<kRowRor8>(y);
+    }
+  }
+  return first;
+}
+
 // The work of one (KV head kvh, split s, request b) workgroup of kWaves waves.
 // LDS comes from the caller: slot ids slot_lds[kWaves][kSuper], wave w's
 // accumulator rows (G * D floats) at red_acc + w * wstride, and red_ml.
@@ -580,28 +630,43 @@ __device__ __forceinline__ void decode_split(const DecodeArgs& a, int kvh, int s
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // before the next pass rewrites the ids
   }
 
-  // Reduce over the token groups: lanes with equal c hold the same elements
-  // (lanes c + LPR grp; with LPR = 8, row_ror:8 first pairs the groups of a row).
+  // Sum over the token groups (lanes c + LPR grp with equal c hold the same
+  // elements). The accumulators, one flat array of G * E per lane, go through
+  // a reduce-scatter: each halving step exchanges one half with the partner
+  // group and adds, so each lane ends with the complete sums of a contiguous
+  // run of NPL of them (within one head, chunk-aligned), stored to LDS as is.
+  // The G row sums are summed over all groups in every lane.
+  constexpr int NV = G * E;
+  constexpr int NPL = NV / (64 / LPR);  // values each lane ends with
+  constexpr int RUN = NPL < Gm::EPC ? NPL : Gm::EPC;  // contiguous elements per store
+  static_assert(NPL % RUN == 0 && E % RUN == 0, "runs stay inside one chunk of one head");
+  float v[NV];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[h * E + e] = st.acc[h][e];
+  const int first = group_reduce_scatter<LPR, NV>(v, lane);  // index of this lane's v[0]
   auto over_groups = [&](float x) {
     if constexpr (LPR == 8) x += dpp<kRowRor8>(x);
     return add_xor32(add_xor16(x));
   };
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.l[h] = over_groups(st.l[h]);
-#pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[h][e] = over_groups(st.acc[h][e]);
-  }
+  for (int h = 0; h < G; ++h) st.l[h] = over_groups(st.l[h]);
   // Hand the wave's (m, l, acc) to LDS; an empty wave leaves m = -inf, l = 0, acc = 0.
-  if (lane < LPR) {
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int k = 0; k < NPL; k += RUN) {
+    const int idx = first + k;
+    const int h = idx / E, ee = idx % E;
+    float* dst = red_acc + wave * wstride + h * D + (c + LPR * (ee / Gm::EPC)) * Gm::EPC +
+                 ee % Gm::EPC;
+    if constexpr (RUN % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < CH; ++k)
+      for (int r = 0; r < RUN; r += 4)
+        *(float4*)(dst + r) = make_float4(v[k + r], v[k + r + 1], v[k + r + 2], v[k + r + 3]);
+    } else {
 #pragma unroll
-        for (int e = 0; e < Gm::EPC; ++e)
-          red_acc[wave * wstride + h * D + (c + LPR * k) * Gm::EPC + e] =
-              st.acc[h][k * Gm::EPC + e];
+      for (int r = 0; r < RUN; ++r) dst[r] = v[k + r];
+    }
   }
   if (lane == 0) {
 #pragma unroll
