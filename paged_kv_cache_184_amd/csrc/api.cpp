@@ -212,9 +212,10 @@ pkv_status pkv_choose_split(int32_t max_len, int32_t batch, int64_t total_len, i
   const int64_t len = max_len > 0 ? max_len : 1;
   int64_t tokens;
   if (batch > 1 && total_len >= 0) {
-    // about two workgroups per CU over all (request, KV head, split) items
+    // about 1.8 workgroups per CU over all (request, KV head, split) items:
+    // T = ceil(total * n_kv_heads / (1.8 * n_cu)), in integers
     const int64_t tot = total_len > 0 ? total_len : 1;
-    tokens = (tot * n_kv_heads + 2 * (int64_t)n_cu - 1) / (2 * (int64_t)n_cu);
+    tokens = (tot * n_kv_heads * 5 + 9 * (int64_t)n_cu - 1) / (9 * (int64_t)n_cu);
   } else {
     // the longest request's workgroups cover the device about once
     int64_t want = (int64_t)n_cu / ((int64_t)batch * n_kv_heads);
