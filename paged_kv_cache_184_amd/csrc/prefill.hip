@@ -13,14 +13,16 @@
 //
 // Per 64-key block:
 //   * K and V rows are gathered through the slot table straight into LDS
-//     (global_load_lds_dwordx4, no registers), row-major with the 16-byte
+//     (16-byte-per-lane buffer loads with the LDS bit, no registers; the
+//     global form for pools past 32-bit offsets), row-major with the 16-byte
 //     chunks of row r XOR-swizzled by r, into a two-stage ring: the next block
-//     is in flight while one is computed. Each wave waits for its own
-//     transfers with an explicit vmcnt; one barrier per block then publishes
-//     the stage and frees the other one. Slot ids arrive the same way two
-//     blocks ahead, so the queue is never drained inside the loop. The ring
-//     (66 KiB) and a 256-register cap let two workgroups share a CU, so one
-//     wave's softmax overlaps the other's MFMAs on each SIMD.
+//     is in flight while one is computed, its transfers spread over the
+//     current block's S^T MFMA groups. Each wave waits for its own transfers
+//     with an explicit vmcnt; one barrier per block then publishes the stage
+//     and frees the other one. Slot ids arrive the same way two blocks ahead,
+//     so the queue is never drained inside the loop. The ring (66 KiB) and a
+//     256-register cap let two workgroups share a CU, so one wave's softmax
+//     overlaps the other's MFMAs on each SIMD.
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand, Q^T held in
 //     registers as the B operand for the whole tile);
@@ -111,6 +113,14 @@ __device__ __forceinline__ int swz8(int r, int c) {
 #define PKV_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define PKV_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
 
+// Buffer descriptor of `bytes` bytes at `base`: no stride, untyped 32-bit
+// data format (the third descriptor word of the gfx9 family); an access past
+// the range reads zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           (int)0x00020000);
+}
+
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -134,8 +144,7 @@ __device__ __forceinline__ u32x2 tr_read(const char* p) {
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
 // One 64-key block for this wave's 32 query rows, taken as two 32-key halves
-// (S, stabiliser check, P and O for one half before the next) so that only one
-// half's scores are live. scale2 > 0 (the caller negates Q for a negative
+// j (key tiles 2j, 2j+1). scale2 > 0 (the caller negates Q for a negative
 // scale and zeroes it for a zero scale), so the largest scaled score is the
 // scaled largest raw score, the scale folds into the exponent's FMA and a
 // masked score (-inf) gives weight 0.
@@ -149,56 +158,107 @@ constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 // the fp32 / bf16 range limits.
 // MASK: the block straddles the causal diagonal or the sequence end (a
 // separate instantiation, so unmasked blocks carry no per-score selects).
-template <int D, int G, bool MASK, typename KV, bool TRACK>
+//
+// xfer(t), t < NT, queues transfer t of the next block; the transfers ride
+// along with the S groups instead of leaving the barrier as one burst, which
+// the CU's memory pipeline takes one at a time while the wave's MFMAs wait
+// behind them in its instruction stream.
+//
+// Issue order. A dependent 16x16x32 MFMA waits about three times the issue
+// interval of its predecessor, and an LDS read about as long as four MFMAs,
+// so every MFMA group has four independent accumulators and its operands are
+// read from LDS one group ahead (explicit scheduling fences keep the order):
+//   S^T:  per (half, k-step) group, the K fragments of the half's two key
+//         tiles, then the four (key tile, query tile) MFMAs;
+//   O^T:  per pair of 16-wide head_dim tiles, four V^T transpose reads, then
+//         the four MFMAs; the first group of a half is read before that
+//         half's softmax, so the reads overlap the exponentials.
+template <int D, int G, bool MASK, typename KV, bool TRACK, int NT, typename X>
 __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
     const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
     float (&m)[2], float (&mseen)[2], bool init, int k0,
-    const int (&limit)[2], float scale2, int lane) {
+    const int (&limit)[2], float scale2, int lane, X&& xfer) {
   using Gm = PGeo<D>;
   constexpr int KS = Gm::KSTEPS;
+  constexpr bool kFp8 = sizeof(KV) == 1;
+  // S groups: bf16 K, one k-step per group; E4M3 K, one 16-byte read holds
+  // the codes of k-steps 2kp and 2kp + 1, widened exactly to bf16 (the Q
+  // fragments are loaded in the same order)
+  constexpr int SG = kFp8 ? KS / 2 : KS;  // S groups per half
+  constexpr int VG = Gm::DT / 2;          // O groups per half
   const int col = lane & 15;
   const int quad = lane >> 4;
   const int s4 = col & 3;
   const u32x4 ones = u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-  // S^T for key tiles 2j, 2j+1 x 2 query tiles
-  auto scores = [&](int j, f32x4 (&s)[2][2]) {
+  const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- S^T = K Q^T for both halves: sc[j][h][n] is key tile 2j+h x query tile n
+  f32x4 sc[2][2][2];
+  auto kread = [&](int g, u32x4 (&kb)[2]) {
+    const int j = g / SG, ks = g % SG;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int kt = 2 * j + h;
-      s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (sizeof(KV) == 2) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 ka = *(const u32x4*)(lds_k + swz<D>(16 * kt + col, 4 * ks + quad));
-          s[h][0] = mfma16(ka, qf[0][ks], s[h][0]);
-          s[h][1] = mfma16(ka, qf[1][ks], s[h][1]);
-        }
-      } else {
-        // E4M3 codes: one 16-byte read holds key row bytes 16 quad + 64 kp ..
-        // +15, the elements of k-steps 2 kp (first 8) and 2 kp + 1, widened
-        // exactly to bf16 (the Q fragments are loaded in the same order)
-#pragma unroll
-        for (int kp = 0; kp < KS / 2; ++kp) {
-          u32x4 k0, k1;
-          fp8x16_to_bf16x16(*(const u32x4*)(lds_k + swz8<D>(16 * kt + col, quad + 4 * kp)), k0,
-                            k1);
-          s[h][0] = mfma16(k0, qf[0][2 * kp], s[h][0]);
-          s[h][1] = mfma16(k0, qf[1][2 * kp], s[h][1]);
-          s[h][0] = mfma16(k1, qf[0][2 * kp + 1], s[h][0]);
-          s[h][1] = mfma16(k1, qf[1][2 * kp + 1], s[h][1]);
-        }
-      }
+      const int row = 16 * (2 * j + h) + col;
+      kb[h] = kFp8 ? *(const u32x4*)(lds_k + swz8<D>(row, quad + 4 * ks))
+                   : *(const u32x4*)(lds_k + swz<D>(row, 4 * ks + quad));
     }
   };
-  // Both halves' S MFMAs are issued first: the second half's run while the
-  // first half's softmax occupies the VALU, and the first half's P.V MFMAs
-  // run while the second half's softmax does. (Interleaving the two with
-  // scheduling groups was measured slower.)
-  f32x4 sc[2][2][2];
-  scores(0, sc[0]);
-  scores(1, sc[1]);
+  auto smfma = [&](int g, const u32x4 (&kb)[2]) {
+    const int j = g / SG, ks = g % SG;
+    if constexpr (kFp8) {
+      u32x4 lo[2], hi[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) fp8x16_to_bf16x16(kb[h], lo[h], hi[h]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          sc[j][h][n] = mfma16(lo[h], qf[n][2 * ks], ks == 0 ? zero : sc[j][h][n]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sc[j][h][n] = mfma16(hi[h], qf[n][2 * ks + 1], sc[j][h][n]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          sc[j][h][n] = mfma16(kb[h], qf[n][ks], ks == 0 ? zero : sc[j][h][n]);
+    }
+  };
+  {
+    u32x4 kb[2][2];
+    kread(0, kb[0]);
+#pragma unroll
+    for (int g = 0; g < 2 * SG; ++g) {
+      if (g + 1 < 2 * SG) kread(g + 1, kb[(g + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // the next block's transfers, spread over the S groups
+#pragma unroll
+      for (int t = g * NT / (2 * SG); t < (g + 1) * NT / (2 * SG); ++t) xfer(t);
+      smfma(g, kb[g & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- V^T fragments: group (j, gv) covers head_dim tiles 2gv, 2gv+1 of keys
+  // 32j .. 32j+31. Column 16dt + 4(s%4) lives in logical chunk 2dt + (s%4)/2,
+  // half (s%2) of the row-major V tile.
+  auto vread = [&](int j, int gv, u32x4 (&vb)[2]) {
+    const int r0 = 32 * j + 4 * quad + (col >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int dt = 2 * gv + e;
+      const int chunk = 2 * dt + (s4 >> 1);
+      const int half = 8 * (s4 & 1);
+      const u32x2 lo = tr_read<D>(lds_v + swz<D>(r0, chunk) + half);
+      const u32x2 hi = tr_read<D>(lds_v + swz<D>(r0 + 16, chunk) + half);
+      vb[e] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  u32x4 vb[2][2];
+  vread(0, 0, vb[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -261,22 +321,20 @@ __device__ __forceinline__ void attend_block(
     // row sums of the rounded P: ones x P^T
     lacc[0] = mfma16(ones, pf[0], lacc[0]);
     lacc[1] = mfma16(ones, pf[1], lacc[1]);
-    // O^T += V^T P^T; V^T fragments by transpose reads of the row-major V tile.
-    // Column 16dt + 4(s%4) lives in logical chunk 2dt + (s%4)/2, half (s%2).
-    const int r0 = 32 * j + 4 * quad + (col >> 2);
-#pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt) {
-      const int chunk = 2 * dt + (s4 >> 1);
-      const int half = 8 * (s4 & 1);
-      const u32x2 lo = tr_read<D>(lds_v + swz<D>(r0, chunk) + half);
-      const u32x2 hi = tr_read<D>(lds_v + swz<D>(r0 + 16, chunk) + half);
-      const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      o[dt][0] = mfma16(va, pf[0], o[dt][0]);
-      o[dt][1] = mfma16(va, pf[1], o[dt][1]);
-    }
-    // keep the two halves apart: hoisting the second half's LDS reads above
-    // the first half's MFMAs would raise the register count past 256
     __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T, the next group's V^T read ahead (across the halves too)
+#pragma unroll
+    for (int gv = 0; gv < VG; ++gv) {
+      const int q = j * VG + gv;  // running group index
+      if (q + 1 < 2 * VG) vread((q + 1) / VG, (q + 1) % VG, vb[(q + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        o[2 * gv + e][0] = mfma16(vb[q & 1][e], pf[0], o[2 * gv + e][0]);
+        o[2 * gv + e][1] = mfma16(vb[q & 1][e], pf[1], o[2 * gv + e][1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -355,7 +413,13 @@ __device__ bool sorted_item(const PrefillArgs& a, int k, int& b, int& kvh, int& 
   return false;  // not reached: the counts cover item
 }
 
-template <int D, int G, typename KV>
+// BUF: the transfers into LDS are buffer loads against descriptors of the
+// layer's K and V pools and the request's slot-table row (byte ranges below
+// 2^32). With the global form, the compiler counts each LDS transfer in
+// flight as an unordered LDS event and turns every wait for an LDS read of
+// the block into a wait for all of them; the buffer form keeps those waits
+// exact, so the fragment reads issued one group ahead stay in flight.
+template <int D, int G, typename KV, bool BUF>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   using Gm = PGeo<D>;
   using Sg = PStore<D, KV>;
@@ -419,16 +483,41 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   const int pch = lane % Sg::CPR;
   const char* kbase = (const char*)a.k + (int64_t)kvh * Sg::ROW;
   const char* vbase = (const char*)a.v + (int64_t)kvh * Sg::ROW;
+  // BUF: every transfer's offset from kbase / vbase is below the span (the
+  // launcher takes this form only when the layer's pool is below 0xF0000000
+  // bytes); the slot-table row's range ends at the tile's last visible key.
+  // A transfer for a block past the end gets offset kNoBlock, past every
+  // range: it reads zeros and touches no memory, and the wait counts stay
+  // the same in every iteration without a branch around the transfers (a
+  // branch there makes the compiler drain all of them before the next LDS
+  // read).
+  constexpr uint32_t kNoBlock = 0xFFFFFFF0u;
+  const uint32_t span = BUF ? (uint32_t)((int64_t)n_slots * row_stride - (int64_t)kvh * Sg::ROW) : 0u;
+  const auto krs = make_rsrc(kbase, span);
+  const auto vrs = make_rsrc(vbase, span);
+  const auto irs = make_rsrc(row, BUF ? 4u * (uint32_t)kv_end : 0u);
+  // one 16-byte transfer per lane from base + off into LDS at dst + 16 lane
+  auto dma16 = [&](const __amdgpu_buffer_rsrc_t& rs, const char* base, auto off, char* dst) {
+    if constexpr (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, PKV_LDS(dst), 16, (uint32_t)off, 0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(PKV_GLB(base + off), PKV_LDS(dst), 16, 0, 0);
+  };
 
   // Slot ids of a block arrive by DMA too (one 4-byte transfer per lane into a
   // per-wave ring in LDS), so every vector-memory operation of the loop is
-  // under the explicit wait counts below. Positions past the end are clamped.
+  // under the explicit wait counts below. Positions past the end are clamped
+  // (global form) or not read (BUF).
   auto id_ring = [&](int ring) -> int* { return ring == 0 ? &id0[wave][0] : &id1[wave][0]; };
   auto stage_ptr = [&](int ring) -> char* { return ring == 0 ? st0 : st1; };
   auto load_ids = [&](int blk, int ring) {
     const int kb = min(blk, nblk - 1) * kBK;
-    const int32_t* src = row + min(kb + lane, kv_end - 1);
-    __builtin_amdgcn_global_load_lds(PKV_GLB(src), PKV_LDS(id_ring(ring)), 4, 0, 0);
+    const int pos = min(kb + lane, kv_end - 1);
+    if constexpr (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, PKV_LDS(id_ring(ring)), 4,
+                                               blk < nblk ? 4u * (uint32_t)pos : kNoBlock, 0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(PKV_GLB(row + pos), PKV_LDS(id_ring(ring)), 4, 0, 0);
   };
   // the logical chunk the tile's swizzle puts at this lane's physical chunk
   auto chunk_of = [&](int rr) {
@@ -437,7 +526,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     else
       return pch ^ (rr & (Sg::CPR - 1));
   };
-  auto offsets = [&](int ring, int64_t (&off)[Sg::NI]) {
+  // BUF: 32-bit offsets from the descriptor bases (fewer live registers
+  // while the transfers are spread over the S phase)
+  using Off = std::conditional_t<BUF, uint32_t, int64_t>;
+  // live: the block exists (BUF; the global form always reads a clamped block)
+  auto offsets = [&](int ring, Off (&off)[Sg::NI], bool live) {
     const int* ids = id_ring(ring);
 #pragma unroll
     for (int i = 0; i < Sg::NI; ++i) {
@@ -445,26 +538,32 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       // unsigned 32 x 32 -> 64-bit product (one multiply-add): the clamped
       // slot is non-negative and the row stride is below 2^24 (at most 65535
       // KV heads of 256 bytes)
-      off[i] = (int64_t)((uint64_t)(uint32_t)clamp_index(ids[rr], n_slots) * (uint32_t)row_stride +
-                         (uint32_t)(16 * chunk_of(rr)));
+      off[i] = (Off)((uint64_t)(uint32_t)clamp_index(ids[rr], n_slots) * (uint32_t)row_stride +
+                     (uint32_t)(16 * chunk_of(rr)));
+      if constexpr (BUF) off[i] = live ? off[i] : kNoBlock;
     }
   };
   // E4M3 pools: this lane's V chunks of the next block, in registers until
   // they are widened into the bf16 V tile
   u32x4 vreg[kFp8 ? Sg::NI : 1];
-  auto issue = [&](int stage, const int64_t (&off)[Sg::NI]) {
+  // transfer t of a block: K rows (t even) or V rows (t odd) 16*wave + RPI*(t/2) ..
+  constexpr int kNT = 2 * Sg::NI;
+  auto issue_one = [&](int stage, const Off (&off)[Sg::NI], int t) {
     char* st = stage_ptr(stage);
+    const int i = t >> 1;
+    const int rbase = 16 * wave + Sg::RPI * i;
+    if ((t & 1) == 0)
+      dma16(krs, kbase, off[i], st + rbase * Sg::ROW);
+    else if constexpr (kFp8 && BUF)
+      vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off[i], 0, 0));
+    else if constexpr (kFp8)
+      vreg[i] = *(const u32x4*)(vbase + off[i]);
+    else
+      dma16(vrs, vbase, off[i], st + Sg::KTILE + rbase * Gm::ROW);
+  };
+  auto issue = [&](int stage, const Off (&off)[Sg::NI]) {
 #pragma unroll
-    for (int i = 0; i < Sg::NI; ++i) {
-      const int rbase = 16 * wave + Sg::RPI * i;
-      __builtin_amdgcn_global_load_lds(PKV_GLB(kbase + off[i]), PKV_LDS(st + rbase * Sg::ROW), 16,
-                                       0, 0);
-      if constexpr (kFp8)
-        vreg[i] = *(const u32x4*)(vbase + off[i]);
-      else
-        __builtin_amdgcn_global_load_lds(PKV_GLB(vbase + off[i]),
-                                         PKV_LDS(st + Sg::KTILE + rbase * Gm::ROW), 16, 0, 0);
-    }
+    for (int t = 0; t < kNT; ++t) issue_one(stage, off, t);
   };
   // E4M3 pools: widen this lane's V chunks (row rr, logical code chunk c ->
   // bf16 chunks 2c, 2c + 1) into the stage's bf16 V tile
@@ -541,16 +640,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     // explicit wait counts are exact: before block i is computed the queue
     // holds, oldest first, S(i+1) D(i) S(i+2), where D(k) = 2*NI tile transfers
     // of block k into stage k % 2 and S(k) = one slot-id transfer for block k
-    // into id ring k % 2. Block indices past the end are clamped, so the counts
-    // never change. E4M3 pools: D(k) is NI K transfers plus NI V loads into
-    // registers, and block i waits for everything in flight (all of it belongs
-    // to block i) before its V is widened into the tile and S(i+2) is queued.
-    int64_t off[Sg::NI];
+    // into id ring k % 2 (past the last block: clamped, or empty under BUF).
+    // E4M3 pools: D(k) is NI K transfers plus NI V loads into registers, and
+    // block i waits for everything in flight (all of it belongs to block i)
+    // before its V is widened into the tile and S(i+2) is queued.
+    Off off[Sg::NI];
     load_ids(0, 0);
     load_ids(1, 1);
     __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    offsets(0, off);
+    offsets(0, off, true);
     issue(0, off);
 
     // One block: wait for its transfers, queue the next ones, attend.
@@ -566,12 +665,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       }
       __builtin_amdgcn_s_barrier();              // ... for every wave; block i-1 is done
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      offsets(u ^ 1, off);
-      issue(u ^ 1, off);  // block i+1 into the stage block i-1 used
+      // block i+1 goes into the stage block i-1 used
+      offsets(u ^ 1, off, i + 1 < nblk);
       const char* st = stage_ptr(u);
-      attend_block<D, G, decltype(masked)::value, KV, decltype(track)::value>(
+      attend_block<D, G, decltype(masked)::value, KV, decltype(track)::value, kNT>(
           st, st + Sg::KTILE, qf, o, lacc, m, mseen, init_pass && i == 0, i * kBK, limit, scale2,
-          lane);
+          lane, [&](int t) { issue_one(u ^ 1, off, t); });
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
     // Blocks that every row sees whole and that end inside the sequence need
@@ -589,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         block(i0 + u, u, std::true_type{});
       }
     }
-    // drain the transfers still in flight (before another pass or the exit)
+    // drain the transfers past the end (before another pass or the exit)
     __builtin_amdgcn_s_waitcnt(PKV_VMCNT(0));
   };
   run_pass(std::false_type{}, true);
@@ -656,12 +755,23 @@ hipError_t prefill_for_dim(PrefillArgs a, hipStream_t stream) {
       grid = dim3((unsigned)blocks, 1, 1);
     }
   }
+  // buffer descriptors span 32-bit offsets: the layer's pool and the slot-table
+  // row (int32 entries) must stay below the no-block offset 0xFFFFFFF0
+  const int64_t pool_bytes = a.n_slots * (int64_t)a.n_kv_heads * D * (int64_t)sizeof(KV);
+  const bool buf = pool_bytes <= 0xF0000000ll && a.stride <= 0x3C000000ll;
+  auto launch = [&](auto gc) {
+    constexpr int GG = decltype(gc)::value;
+    if (buf)
+      prefill_kernel<D, GG, KV, true><<<grid, kThreads, 0, stream>>>(a);
+    else
+      prefill_kernel<D, GG, KV, false><<<grid, kThreads, 0, stream>>>(a);
+  };
   switch (g) {
-    case 1: prefill_kernel<D, 1, KV><<<grid, kThreads, 0, stream>>>(a); break;
-    case 2: prefill_kernel<D, 2, KV><<<grid, kThreads, 0, stream>>>(a); break;
-    case 4: prefill_kernel<D, 4, KV><<<grid, kThreads, 0, stream>>>(a); break;
-    case 8: prefill_kernel<D, 8, KV><<<grid, kThreads, 0, stream>>>(a); break;
-    case 16: prefill_kernel<D, 16, KV><<<grid, kThreads, 0, stream>>>(a); break;
+    case 1: launch(std::integral_constant<int, 1>{}); break;
+    case 2: launch(std::integral_constant<int, 2>{}); break;
+    case 4: launch(std::integral_constant<int, 4>{}); break;
+    case 8: launch(std::integral_constant<int, 8>{}); break;
+    case 16: launch(std::integral_constant<int, 16>{}); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
