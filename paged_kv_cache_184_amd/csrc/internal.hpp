@@ -101,7 +101,7 @@ struct PrefillArgs {
   int32_t causal;
   void* out;
   const float* kv_scale;  // E4M3 pools: this layer's (k_scale, v_scale)
-  int32_t sorted;         // set by the launcher: 1-D grid in decreasing tile cost
+  int32_t sorted;         // set by the launcher: 1-D grid, request by request, longest tile first
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

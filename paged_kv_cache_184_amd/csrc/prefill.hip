@@ -39,9 +39,10 @@
 //     those lanes at keys base+4g+0..3 and columns 16dt+4(s%4) gives every
 //     lane the 4 keys it needs at its own column.
 // Only blocks that straddle the causal diagonal or the sequence end are
-// masked. Up to 64 requests, the (request, tile) items run in decreasing cost
-// over the whole batch (a 1-D launch, KV head fastest); larger batches use a
-// (tile, KV head, request) grid, each request's longest tiles first.
+// masked. Up to 64 requests, the (request, tile) items run request by request
+// (longest-tile order) and longest tile first within a request (a 1-D launch,
+// KV head fastest); larger batches use a (tile, KV head, request) grid, each
+// request's longest tiles first.
 #include <math.h>
 
 #include <algorithm>
@@ -178,7 +179,7 @@ __device__ __forceinline__ void attend_block(
     const char* __restrict__ lds_k, const char* __restrict__ lds_v,
     const u32x4 (&qf)[2][PGeo<D>::KSTEPS], f32x4 (&o)[PGeo<D>::DT][2], f32x4 (&lacc)[2],
     float (&m)[2], float (&mseen)[2], bool init, int k0,
-    const int (&limit)[2], float scale2, int lane, X&& xfer) {
+    const int (&limit)[2], int wlim, float scale2, int lane, X&& xfer) {
   using Gm = PGeo<D>;
   constexpr int KS = Gm::KSTEPS;
   constexpr bool kFp8 = sizeof(KV) == 1;
@@ -192,6 +193,14 @@ __device__ __forceinline__ void attend_block(
   const int s4 = col & 3;
   const u32x4 ones = u32x4{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
   const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+  // MASK: a half whose first key is past the wave's last visible key (wlim,
+  // wave-uniform) adds nothing and is skipped (if half 0 is, so is half 1);
+  // the transfers and the operand reads stay unconditional
+  bool live[2] = {true, true};
+  if constexpr (MASK) {
+    live[0] = k0 <= wlim;
+    live[1] = k0 + 32 <= wlim;
+  }
 
   // ---- S^T = K Q^T for both halves: sc[j][h][n] is key tile 2j+h x query tile n
   f32x4 sc[2][2][2];
@@ -237,7 +246,7 @@ __device__ __forceinline__ void attend_block(
       // the next block's transfers, spread over the S groups
 #pragma unroll
       for (int t = g * NT / (2 * SG); t < (g + 1) * NT / (2 * SG); ++t) xfer(t);
-      smfma(g, kb[g & 1]);
+      if (live[g / SG]) smfma(g, kb[g & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -262,6 +271,7 @@ __device__ __forceinline__ void attend_block(
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    if (!live[j]) break;
     f32x4 (&s)[2][2] = sc[j];
     // mask (blocks on the causal diagonal or the sequence end only), then the
     // stabiliser check on the raw maxima
@@ -341,27 +351,34 @@ __device__ __forceinline__ void attend_block(
 // Largest batch whose tiles are ordered by cost (one request per lane of a wave).
 constexpr int kSortedMaxBatch = 64;
 
-// Work item k of the sorted launch order (batch <= kSortedMaxBatch): items are
-// the (request, query tile) pairs in decreasing cost, the cost of a tile being
-// the 64-key blocks it reads (ties in request order, then decreasing tile), and
-// the KV head is fastest, so the heads of one item run side by side and, with
-// the KV head count a multiple of 8, each XCD serves one head of every request.
-// Greedy dispatch of the longest tiles first leaves only short ones for the
-// end of the launch. Every wave computes the same answer from the request
-// words (one request per lane): the cost c of item k is the largest c with
-// more than k tiles of cost >= c, found by bisection on counts that are closed
-// forms per request. Returns false when k is past the last item.
+// Work item k of the ordered launch (batch <= kSortedMaxBatch): items are the
+// (request, query tile) pairs, request by request in decreasing cost of the
+// request's longest tile (the 64-key blocks it reads; ties in request order),
+// each request's tiles longest first; the KV head is fastest, so the heads of
+// one item run side by side and, with the KV head count a multiple of 8, each
+// XCD serves one head. Keeping a request's tiles together keeps the K/V that
+// the tiles in flight share within an XCD's L2 (all requests' K/V of one head
+// at once overflow it), and the shortest requests' short tiles end the launch.
+// Every wave computes the same answer from the request words (one request per
+// lane). Returns false when k is past the last item; otherwise words holds
+// request b's raw qo_indptr[b], qo_indptr[b+1], seq_lens[b] and
+// req_pool_indices[b] (taken from the lane that loaded them).
 template <int BQ>
-__device__ bool sorted_item(const PrefillArgs& a, int k, int& b, int& kvh, int& tile) {
+__device__ bool sorted_item(const PrefillArgs& a, int k, int& b, int& kvh, int& tile,
+                            int (&words)[4]) {
   const int lane = threadIdx.x & 63;
   const int item = k / a.n_kv_heads;
   kvh = k - item * a.n_kv_heads;
   // this lane's request, clamped as the tile code clamps it
   int n = 0, P = 0, nt = 0, cmax = 0;
+  int raw[4] = {0, 0, 0, 0};
   if (lane < a.batch) {
-    const int q0 = a.qo_indptr[lane];
-    const int q1 = a.qo_indptr[lane + 1];
-    int L = a.seq_lens[lane];
+    raw[0] = a.qo_indptr[lane];
+    raw[1] = a.qo_indptr[lane + 1];
+    raw[2] = a.seq_lens[lane];
+    raw[3] = a.req_pool_indices[lane];
+    const int q0 = raw[0], q1 = raw[1];
+    int L = raw[2];
     L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
     n = q1 - q0;
     n = n < 0 ? 0 : (n > L ? L : n);
@@ -372,45 +389,21 @@ __device__ bool sorted_item(const PrefillArgs& a, int k, int& b, int& kvh, int& 
       cmax = (last_end + kBK - 1) / kBK;
     }
   }
-  // tiles of this lane's request that read at least c blocks
-  auto count = [&](int c) -> int {
-    if (nt == 0) return 0;
-    if (!a.causal) return cmax >= c ? nt : 0;
-    const int64_t thr = (int64_t)kBK * (c - 1) - P;  // tile t reads >= c blocks iff its
-    if (thr < 0) return nt;                           // last key P + min((t+1) BQ, n) - 1
-    if (n <= thr) return 0;                           // is at least thr
-    return max(0, nt - (int)(thr / BQ));
-  };
-  auto wave_add = [](int x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
-    return x;
-  };
-  int hi = cmax;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) hi = max(hi, __shfl_xor(hi, off));
-  if (item >= wave_add(nt)) return false;
-  // count(lo) > item >= count(hi)
-  int lo = 1;
-  hi += 1;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (wave_add(count(mid)) > item) lo = mid; else hi = mid;
+  // the tiles of the requests ordered before this lane's request
+  int before = 0;
+  for (int i = 0; i < a.batch; ++i) {
+    const int ci = __shfl(cmax, i);
+    const int ni = __shfl(nt, i);
+    before += ci > cmax || (ci == cmax && i < lane) ? ni : 0;
   }
-  const int above = count(lo + 1);            // this request's tiles costlier than lo
-  const int m = count(lo) - above;            // its tiles of cost exactly lo
-  int o = item - wave_add(above);             // rank among the tiles of cost lo
-  b = 0;
-  for (int i = 0; i < a.batch; ++i) {         // uniform walk over the requests
-    const int mi = __shfl(m, i);
-    if (o < mi) {
-      b = i;
-      tile = __shfl(nt - above, i) - 1 - o;   // decreasing tile index within the cost
-      return true;
-    }
-    o -= mi;
-  }
-  return false;  // not reached: the counts cover item
+  const bool mine = lane < a.batch && item >= before && item < before + nt;
+  const uint64_t owner = __builtin_amdgcn_ballot_w64(mine);
+  if (owner == 0) return false;
+  b = __builtin_ctzll(owner);
+  tile = __shfl(nt - 1 - (item - before), b);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) words[w] = __shfl(raw[w], b);
+  return true;
 }
 
 // BUF: the transfers into LDS are buffer loads against descriptors of the
@@ -441,24 +434,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // computed in scalar registers, not read back from a vector lane per transfer
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int kvh, b, tile;
+  int q0, q1, L, r_raw;  // the request's words
   if (a.sorted) {
-    if (!sorted_item<BQ>(a, blockIdx.x, b, kvh, tile)) return;
+    int w[4];
+    if (!sorted_item<BQ>(a, blockIdx.x, b, kvh, tile, w)) return;
     b = __builtin_amdgcn_readfirstlane(b);
     kvh = __builtin_amdgcn_readfirstlane(kvh);
     tile = __builtin_amdgcn_readfirstlane(tile);
+    q0 = __builtin_amdgcn_readfirstlane(w[0]);
+    q1 = __builtin_amdgcn_readfirstlane(w[1]);
+    L = __builtin_amdgcn_readfirstlane(w[2]);
+    r_raw = __builtin_amdgcn_readfirstlane(w[3]);
   } else {
     kvh = blockIdx.y;
     b = blockIdx.z;
     tile = gridDim.x - 1 - blockIdx.x;  // longest work of the request first
+    // scalar loads, all in flight before any is used
+    q0 = load_uniform(a.qo_indptr + b);
+    q1 = load_uniform(a.qo_indptr + b + 1);
+    L = load_uniform(a.seq_lens + b);
+    r_raw = load_uniform(a.req_pool_indices + b);
+    asm volatile("" : "+s"(q0), "+s"(q1), "+s"(L), "+s"(r_raw));
   }
   const int t0 = tile * BQ;
-
-  // the request's words as scalar loads, all in flight before any is used
-  int q0 = load_uniform(a.qo_indptr + b);
-  int q1 = load_uniform(a.qo_indptr + b + 1);
-  int L = load_uniform(a.seq_lens + b);
-  int r_raw = load_uniform(a.req_pool_indices + b);
-  asm volatile("" : "+s"(q0), "+s"(q1), "+s"(L), "+s"(r_raw));
   int n_new = q1 - q0;
   if (t0 >= n_new) return;
   L = L < 0 ? 0 : (L > a.stride ? (int)a.stride : L);
@@ -604,6 +602,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
                                              : 64 * ks + 16 * quad));
     limit[n] = a.causal ? min(P + tc, L - 1) : L - 1;
   }
+  // the wave's last visible key: that of its last row (wave-uniform)
+  const int wlim =
+      a.causal ? min(P + min(t0 + (wave * 32 + 31) / G, n_new - 1), L - 1) : L - 1;
 
   // a negative scale is applied as -scale on -Q (bf16 negation is exact), a
   // zero scale as scale 1 on Q = 0 (every score is exactly 0 either way)
@@ -669,8 +670,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
       offsets(u ^ 1, off, i + 1 < nblk);
       const char* st = stage_ptr(u);
       attend_block<D, G, decltype(masked)::value, KV, decltype(track)::value, kNT>(
-          st, st + Sg::KTILE, qf, o, lacc, m, mseen, init_pass && i == 0, i * kBK, limit, scale2,
-          lane, [&](int t) { issue_one(u ^ 1, off, t); });
+          st, st + Sg::KTILE, qf, o, lacc, m, mseen, init_pass && i == 0, i * kBK, limit, wlim,
+          scale2, lane, [&](int t) { issue_one(u ^ 1, off, t); });
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     };
     // Blocks that every row sees whole and that end inside the sequence need

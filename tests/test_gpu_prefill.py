@@ -203,7 +203,7 @@ def test_poisoned_pool_stays_finite():
 
 @pytest.mark.parametrize("n_req,causal", [(64, True), (64, False), (70, True)])
 def test_many_requests_every_row(n_req, causal):
-    """Up to 64 requests the tiles run in decreasing cost over the whole batch
+    """Up to 64 requests the tiles run request by request, longest tile first
     (a 1-D launch whose work items are found per workgroup); above 64 in the
     per-request grid. Lengths mix empty requests, one-token requests, tails
     around the tile and the 64-key block, and prefixes: every row must be
