@@ -39,9 +39,11 @@
  *
  * Memory safety: kernels clamp every device-supplied index to the buffer it
  * addresses (slots to [0, n_slots), request rows to [0, n_req_rows), positions
- * to [0, stride), packed rows to [0, total_q)), so malformed metadata gives
- * undefined values but never an out-of-bounds access. pkv_validate_meta
- * reports such metadata.
+ * to [0, stride), packed rows to [0, total_q)), or, for the prefill kernel's
+ * K/V and slot-id reads, read through buffer descriptors spanning exactly the
+ * layer's pool and the request's table row (an access past the range reads
+ * zeros), so malformed metadata gives undefined values but never an
+ * out-of-bounds access. pkv_validate_meta reports such metadata.
  */
 #ifndef PKV_H
 #define PKV_H

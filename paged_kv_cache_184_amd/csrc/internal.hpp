@@ -102,6 +102,7 @@ struct PrefillArgs {
   void* out;
   const float* kv_scale;  // E4M3 pools: this layer's (k_scale, v_scale)
   int32_t sorted;         // set by the launcher: 1-D grid, request by request, longest tile first
+  int32_t row_shift;      // set by the launcher: log2 of the row stride in bytes, or -1
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

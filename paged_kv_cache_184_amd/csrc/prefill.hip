@@ -530,15 +530,34 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // live: the block exists (BUF; the global form always reads a clamped block)
   auto offsets = [&](int ring, Off (&off)[Sg::NI], bool live) {
     const int* ids = id_ring(ring);
+    if constexpr (BUF) {
+      // no clamp: the descriptor's range check keeps any slot id in bounds
+      // (an id past the pool reads zeros); a shift where the row stride is a
+      // power of two (a 32-bit multiply is a quarter-rate instruction)
+      uint32_t base[Sg::NI];
+      if (a.row_shift >= 0) {
 #pragma unroll
-    for (int i = 0; i < Sg::NI; ++i) {
-      const int rr = 16 * wave + Sg::RPI * i + prow;
-      // unsigned 32 x 32 -> 64-bit product (one multiply-add): the clamped
-      // slot is non-negative and the row stride is below 2^24 (at most 65535
-      // KV heads of 256 bytes)
-      off[i] = (Off)((uint64_t)(uint32_t)clamp_index(ids[rr], n_slots) * (uint32_t)row_stride +
-                     (uint32_t)(16 * chunk_of(rr)));
-      if constexpr (BUF) off[i] = live ? off[i] : kNoBlock;
+        for (int i = 0; i < Sg::NI; ++i)
+          base[i] = (uint32_t)ids[16 * wave + Sg::RPI * i + prow] << a.row_shift;
+      } else {
+#pragma unroll
+        for (int i = 0; i < Sg::NI; ++i)
+          base[i] = (uint32_t)ids[16 * wave + Sg::RPI * i + prow] * (uint32_t)row_stride;
+      }
+#pragma unroll
+      for (int i = 0; i < Sg::NI; ++i)
+        off[i] = live ? base[i] + (uint32_t)(16 * chunk_of(16 * wave + Sg::RPI * i + prow))
+                      : kNoBlock;
+    } else {
+#pragma unroll
+      for (int i = 0; i < Sg::NI; ++i) {
+        const int rr = 16 * wave + Sg::RPI * i + prow;
+        // unsigned 32 x 32 -> 64-bit product (one multiply-add): the clamped
+        // slot is non-negative and the row stride is below 2^24 (at most
+        // 65535 KV heads of 256 bytes)
+        off[i] = (Off)((uint64_t)(uint32_t)clamp_index(ids[rr], n_slots) * (uint32_t)row_stride +
+                       (uint32_t)(16 * chunk_of(rr)));
+      }
     }
   };
   // E4M3 pools: this lane's V chunks of the next block, in registers until
@@ -760,6 +779,9 @@ hipError_t prefill_for_dim(PrefillArgs a, hipStream_t stream) {
   // row (int32 entries) must stay below the no-block offset 0xFFFFFFF0
   const int64_t pool_bytes = a.n_slots * (int64_t)a.n_kv_heads * D * (int64_t)sizeof(KV);
   const bool buf = pool_bytes <= 0xF0000000ll && a.stride <= 0x3C000000ll;
+  // a (slot, KV head) row's byte stride as a shift when it is a power of two
+  const int64_t rs = (int64_t)a.n_kv_heads * D * (int64_t)sizeof(KV);
+  a.row_shift = (rs & (rs - 1)) == 0 ? __builtin_ctzll((unsigned long long)rs) : -1;
   auto launch = [&](auto gc) {
     constexpr int GG = decltype(gc)::value;
     if (buf)
