@@ -127,10 +127,28 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Byte offset of logical 16-byte chunk c of row r in a swizzled tile.
+// Byte offset of logical 16-byte chunk c of row r in a swizzled K tile: the
+// 16 rows that one K fragment read takes at one chunk position hit 16
+// distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   return r * PGeo<D>::ROW + 16 * (c ^ (r & (PGeo<D>::CPR - 1)));
+}
+
+// The XOR that places row r's chunks in a V tile. A V^T transpose read takes,
+// in each half of the wave, 8 rows at the chunk pair (2dt, 2dt+1); for those
+// 16 (row, chunk) pieces to hit 16 distinct bank groups the 8 rows must land
+// in 8 distinct chunk pairs (D = 128: XOR by 2r; D = 64, two 128-byte rows
+// per 256-byte bank line: XOR by 2 ((r/2) % 4) within each line half).
+template <int D>
+__device__ __forceinline__ int vxor(int r) {
+  return D == 128 ? (2 * r) & 15 : 2 * ((r >> 1) & 3);
+}
+
+// Byte offset of logical 16-byte chunk c of row r in a swizzled V tile.
+template <int D>
+__device__ __forceinline__ int swzv(int r, int c) {
+  return r * PGeo<D>::ROW + 16 * (c ^ vxor<D>(r));
 }
 
 template <int D>
@@ -261,8 +279,8 @@ __device__ __forceinline__ void attend_block(
       const int dt = 2 * gv + e;
       const int chunk = 2 * dt + (s4 >> 1);
       const int half = 8 * (s4 & 1);
-      const u32x2 lo = tr_read<D>(lds_v + swz<D>(r0, chunk) + half);
-      const u32x2 hi = tr_read<D>(lds_v + swz<D>(r0 + 16, chunk) + half);
+      const u32x2 lo = tr_read<D>(lds_v + swzv<D>(r0, chunk) + half);
+      const u32x2 hi = tr_read<D>(lds_v + swzv<D>(r0 + 16, chunk) + half);
       vb[e] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   };
@@ -563,6 +581,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
   // E4M3 pools: this lane's V chunks of the next block, in registers until
   // they are widened into the bf16 V tile
   u32x4 vreg[kFp8 ? Sg::NI : 1];
+  // bf16 pools: per transfer, 16 x (K chunk XOR V chunk) of this lane's row
+  // (the physical chunk pch holds logical chunk pch ^ (rr % CPR) in K and
+  // pch ^ vxor(rr) in V)
+  uint32_t vmove[Sg::NI];
+#pragma unroll
+  for (int i = 0; i < Sg::NI; ++i) {
+    const int rr = 16 * wave + Sg::RPI * i + prow;
+    vmove[i] = kFp8 ? 0u : 16u * (uint32_t)((rr & (Sg::CPR - 1)) ^ vxor<D>(rr));
+  }
   // transfer t of a block: K rows (t even) or V rows (t odd) 16*wave + RPI*(t/2) ..
   constexpr int kNT = 2 * Sg::NI;
   auto issue_one = [&](int stage, const Off (&off)[Sg::NI], int t) {
@@ -571,12 +598,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
     const int rbase = 16 * wave + Sg::RPI * i;
     if ((t & 1) == 0)
       dma16(krs, kbase, off[i], st + rbase * Sg::ROW);
-    else if constexpr (kFp8 && BUF)
+    else if constexpr (!kFp8)
+      // bf16 V rows land under the V swizzle: the offset's chunk bits (below
+      // the 128-byte-aligned row base) move from this lane's K chunk to its V chunk
+      dma16(vrs, vbase, off[i] ^ (Off)vmove[i], st + Sg::KTILE + rbase * Gm::ROW);
+    else if constexpr (BUF)
       vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off[i], 0, 0));
-    else if constexpr (kFp8)
-      vreg[i] = *(const u32x4*)(vbase + off[i]);
     else
-      dma16(vrs, vbase, off[i], st + Sg::KTILE + rbase * Gm::ROW);
+      vreg[i] = *(const u32x4*)(vbase + off[i]);
   };
   auto issue = [&](int stage, const Off (&off)[Sg::NI]) {
 #pragma unroll
@@ -593,8 +622,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a) {
         const int c = chunk_of(rr);
         u32x4 lo, hi;
         fp8x16_to_bf16x16(vreg[i], lo, hi);
-        *(u32x4*)(vt + swz<D>(rr, 2 * c)) = lo;
-        *(u32x4*)(vt + swz<D>(rr, 2 * c + 1)) = hi;
+        *(u32x4*)(vt + swzv<D>(rr, 2 * c)) = lo;
+        *(u32x4*)(vt + swzv<D>(rr, 2 * c + 1)) = hi;
       }
     }
   };
