@@ -15,7 +15,8 @@
 //   * K and V rows are gathered through the slot table straight into LDS
 //     (16-byte-per-lane buffer loads with the LDS bit, no registers; the
 //     global form for pools past 32-bit offsets), row-major with the 16-byte
-//     chunks of row r XOR-swizzled by r, into a two-stage ring: the next block
+//     chunks of row r XOR-swizzled (K by r, V by 2r: each tile's reads then
+//     meet no LDS bank conflict), into a two-stage ring: the next block
 //     is in flight while one is computed, its transfers spread over the
 //     current block's S^T MFMA groups. Each wave waits for its own transfers
 //     with an explicit vmcnt; one barrier per block then publishes the stage
