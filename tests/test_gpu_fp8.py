@@ -163,7 +163,8 @@ def test_b1_32k_fp8():
 
 @pytest.mark.parametrize("hq,hkv,d,causal", [(32, 8, 128, True), (32, 8, 128, False),
                                              (16, 4, 64, True), (8, 8, 128, True),
-                                             (64, 4, 128, True), (32, 2, 64, False)])
+                                             (64, 4, 128, True), (32, 2, 64, False),
+                                             (12, 3, 128, True), (10, 5, 64, True)])
 def test_prefill_fp8_parity(hq, hkv, d, causal):
     lens = np.array([300, 70, 1, 129, 700, 64, 5])
     n_new = np.array([64, 70, 1, 33, 200, 0, 5])

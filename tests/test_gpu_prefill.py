@@ -112,6 +112,17 @@ def test_groups_and_dims(g, d):
     check_batch(b, 220 + g, layer=1)
 
 
+@pytest.mark.parametrize("hkv,g,d", [(3, 4, 128), (5, 2, 64), (3, 1, 128)])
+def test_kv_head_counts_not_a_power_of_two(hkv, g, d):
+    """Row strides of 3 x 256, 5 x 128 and 3 x 256 bytes: slot offsets by a
+    32-bit multiply instead of a shift, V chunks moved on row bases that are
+    only 128-byte aligned (D = 64)."""
+    b = W.custom(f"hkv{hkv}g{g}d{d}", n_layers=1, n_slots=8192, n_q_heads=g * hkv,
+                 n_kv_heads=hkv, head_dim=d, dtype="bf16", seq_lens=[260, 97, 1, 140],
+                 n_new=[120, 97, 1, 33], seed=290 + hkv + d)
+    check_batch(b, 291 + hkv + d)
+
+
 def test_packed_prefill_reduced():
     """The packed-prefill workload's structure with every row checked: 3 of its
     8 requests, new tokens and prefixes trimmed so the oracle runs in seconds."""
