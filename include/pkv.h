@@ -36,6 +36,9 @@
  * and prefill entry points and pkv_kv_store; there q, the new K/V rows and the
  * output are BF16 (P4, bullet on the fp8 MMA test kernel of the attention kernels; the
  * code format is the OCP 8-bit floating point E4M3 encoding).
+ * The tuned paths are BF16 and FP8_E4M3. F32 decode is a precision path:
+ * correct for every supported shape, but it reads one 16-token tile at a time
+ * (no prefetch across tiles) and spills registers at group size 16.
  *
  * Memory safety: kernels clamp every device-supplied index to the buffer it
  * addresses (slots to [0, n_slots), request rows to [0, n_req_rows), positions
