@@ -3,9 +3,9 @@
 The prefill kernel addresses K/V through buffer descriptors (32-bit byte
 offsets) while a layer's pool stays below 0xF0000000 bytes, and through
 64-bit global addresses above that. These pools hold 2^32 bytes per layer
-(2^21 bf16 slots or 2^22 E4M3 slots of 8 KV heads x 128), so the requests'
-pages, spread over the whole pool, reach offsets near 4 GiB on the second
-path. Only the live slots get values (unreferenced ones hold NaN or NaN
+(8 KV heads of head_dim 128 or 64: 2^21 or 2^22 bf16 slots, 2^22 or 2^23
+E4M3 slots), so the requests' pages, spread over the whole pool, reach
+offsets near 4 GiB on the second path. Only the live slots get values (unreferenced ones hold NaN or NaN
 codes); the oracle sees those slots compacted under a remapped table, which
 leaves its result unchanged.
 """
@@ -41,19 +41,21 @@ def compact_table(b):
     return live, r2t
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_prefill_pool_past_32bit_offsets(kv):
-    n_slots = 1 << (21 if kv == "bf16" else 22)
-    b = W.custom(f"large_pool_{kv}", n_layers=1, n_slots=n_slots, n_q_heads=32, n_kv_heads=8,
-                 head_dim=128, dtype="bf16", seq_lens=LENS, n_new=N_NEW, seed=700)
+def test_prefill_pool_past_32bit_offsets(kv, d):
+    # 2^32 bytes per layer: 8 heads x d elements of 2 (bf16) or 1 (E4M3) bytes per slot
+    n_slots = (1 << 32) // (8 * d * (2 if kv == "bf16" else 1))
+    b = W.custom(f"large_pool_{kv}_{d}", n_layers=1, n_slots=n_slots, n_q_heads=32,
+                 n_kv_heads=8, head_dim=d, dtype="bf16", seq_lens=LENS, n_new=N_NEW, seed=700)
     live, r2t_c = compact_table(b)
-    say(f"  {kv}: {n_slots} slots per layer, highest live slot {int(live.max())}")
+    say(f"  {kv}, head_dim {d}: {n_slots} slots per layer, highest live slot {int(live.max())}")
     assert live.max() >= n_slots // 2
-    kv_live = W.normal_values((2, live.size, 8, 128), 701, "bf16")
-    q = W.normal_values((b.total_q, 32, 128), 702, "bf16")
-    k_new = W.normal_values((b.total_q, 8, 128), 703, "bf16")
-    v_new = W.normal_values((b.total_q, 8, 128), 704, "bf16")
-    shape = (1, n_slots, 8, 128)
+    kv_live = W.normal_values((2, live.size, 8, d), 701, "bf16")
+    q = W.normal_values((b.total_q, 32, d), 702, "bf16")
+    k_new = W.normal_values((b.total_q, 8, d), 703, "bf16")
+    v_new = W.normal_values((b.total_q, 8, d), 704, "bf16")
+    shape = (1, n_slots, 8, d)
     idx = to_dev(live)
     if kv == "bf16":
         scales = None
@@ -98,4 +100,4 @@ def test_prefill_pool_past_32bit_offsets(kv):
         assert np.array_equal(k_after.numpy(), kp[0]) and np.array_equal(v_after.numpy(), vp[0])
         ref = O.prefill_attention_fp8(q, kp, vp, scales, 0, r2t_c, b.req_pool_indices,
                                       b.seq_lens, b.qo_indptr, b.scale, causal=True)
-    compare(got, ref, "bf16", f"prefill over a 4 GiB {kv} layer pool")
+    compare(got, ref, "bf16", f"prefill over a 4 GiB {kv} layer pool, head_dim {d}")
