@@ -7,7 +7,8 @@ groups with edge lengths (a suffix of one key, no suffix at all, a one-member
 group, a zero-length prefix) for g = 1, 2, 4, 8 and 16, head_dim 64,
 padded rows, determinism, agreement with the plain decode, and a check that
 only the first member's prefix table entries are read; groups of many members
-(ten column tiles) and a member with a different prefix length.
+(ten column tiles) and a member with a different prefix length; capture into
+a HIP graph and replay.
 """
 
 import dataclasses
@@ -155,3 +156,39 @@ def test_prefix_read_through_first_member_only():
     out = run_cascade(db, groups_for(b, [[0, 1, 2, 3]], [P]), ops.split_cfg(8, 0, 256))
     # the reference reads the intact tables
     compare(out.float().cpu().numpy(), oracle(b, vals), "bf16", "prefix via first member")
+
+
+def test_cascade_graph_replay():
+    """Cascade decode captured once into a HIP graph and replayed with q
+    rewritten in place: every replay bit-identical to the same call run
+    eagerly."""
+    lens = [900, 700, 1200, 300]
+    b = shared_batch("cascade_graph", lens, [[0, 1, 2]], [256], 560)
+    vals = W.host_values(b, 561)
+    db = DeviceBatch(b, vals)
+    split = ops.split_cfg(8, 0, 256)
+    groups = groups_for(b, [[0, 1, 2]], [256])
+    meta = db.meta()
+    ws_graph = ops.alloc_decode_workspace(b.batch, b.n_q_heads, b.head_dim, split.max_splits)
+    out_graph = torch.empty_like(db.q)
+    call = ops.prepare_cascade_decode(db.q, db.k_pool, db.v_pool, 0, meta, groups, b.scale, split,
+                                      ws_graph, out_graph)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for step in range(3):
+        say(f"cascade graph replay {step}")
+        if step > 0:
+            x = torch.from_numpy(W.normal_values(tuple(db.q.shape), 570 + step, "bf16"))
+            db.q.copy_(x.to(DEV, torch.bfloat16))
+        out_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        out_eager = run_cascade(db, groups, split)
+        assert torch.equal(out_graph.view(torch.int16), out_eager.view(torch.int16)), step
+        if step == 0:
+            compare(out_graph.float().cpu().numpy(), oracle(b, vals), "bf16",
+                    "graph-replayed cascade")
