@@ -160,30 +160,39 @@ def test_decode_step_graph_replay_with_in_place_metadata(kv):
             compare(A.out.float().cpu().numpy(), ref, "bf16", f"graph step {step} ({kv})")
 
 
-def test_prefill_step_graph_replay():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_step_graph_replay(kv):
     """The prefill step (index step for the new tokens' locations, their store,
     packed causal prefill) captured once and replayed with new q / k / v values
     written in place between replays: every replay bit-identical to the same
     calls run eagerly on a twin (output and both pools), the first also against
-    the oracle."""
+    the oracle. bf16 pools, and E4M3 code pools (quantising store, per-layer
+    scales read by the kernels at run time)."""
     lens = np.array([300, 77, 640])
     n_new = np.array([100, 77, 130])
     b = W.custom("graph_prefill", n_layers=1, n_slots=1 << 13, n_q_heads=32, n_kv_heads=8,
                  head_dim=128, dtype="bf16", seq_lens=lens, n_new=n_new, seed=420)
     vals = W.host_values(b, 421)
+    scales = np.float32([[0.02, 2.0 ** -6]])
 
     class Twin:
         def __init__(self):
             self.db = DeviceBatch(b, vals)
-            self.loc = torch.empty(b.total_q, dtype=torch.int32, device=DEV)
-            self.out = torch.empty_like(self.db.q)
-            meta = self.db.meta(with_qo=True)
             d = self.db
+            self.scales = None
+            if kv == "fp8":
+                self.scales = torch.from_numpy(scales).to(DEV)
+                d.k_pool = torch.from_numpy(O.quantize(vals.k_pool, scales[0, 0])).to(DEV)
+                d.v_pool = torch.from_numpy(O.quantize(vals.v_pool, scales[0, 1])).to(DEV)
+            self.loc = torch.empty(b.total_q, dtype=torch.int32, device=DEV)
+            self.out = torch.empty_like(d.q)
+            meta = d.meta(with_qo=True)
             self.calls = [
                 ops.prepare_metadata(meta, ops.PKV_MODE_PREFILL, None, None, self.loc, None),
-                ops.prepare_kv_store(d.k_pool, d.v_pool, 0, d.k_new, d.v_new, self.loc),
+                ops.prepare_kv_store(d.k_pool, d.v_pool, 0, d.k_new, d.v_new, self.loc,
+                                     kv_scales=self.scales),
                 ops.prepare_prefill(d.q, d.k_pool, d.v_pool, 0, meta, b.max_q_len, b.scale,
-                                    True, self.out),
+                                    True, self.out, kv_scales=self.scales),
             ]
 
         def run(self):
@@ -203,7 +212,7 @@ def test_prefill_step_graph_replay():
         A.run()
     torch.cuda.synchronize()
     for step in range(3):
-        say(f"prefill graph replay {step}")
+        say(f"prefill graph replay {step} ({kv})")
         if step > 0:
             for j, t in enumerate(("q", "k_new", "v_new")):
                 x = torch.from_numpy(W.normal_values(tuple(getattr(A.db, t).shape),
@@ -219,10 +228,19 @@ def test_prefill_step_graph_replay():
         if step == 0:
             loc = O.prefill_locations(b.req_to_token, b.req_pool_indices, b.seq_lens,
                                       b.qo_indptr)
-            kp, vp = O.kv_store(vals.k_pool, vals.v_pool, 0, vals.k_new, vals.v_new, loc)
-            ref = O.prefill_attention(vals.q, kp, vp, 0, b.req_to_token, b.req_pool_indices,
-                                      b.seq_lens, b.qo_indptr, b.scale, causal=True)
-            compare(A.out.float().cpu().numpy(), ref, "bf16", "graph-replayed prefill")
+            if kv == "fp8":
+                kp, vp = O.kv_store_fp8(O.quantize(vals.k_pool, scales[0, 0]),
+                                        O.quantize(vals.v_pool, scales[0, 1]), 0, vals.k_new,
+                                        vals.v_new, loc, scales)
+                ref = O.prefill_attention_fp8(vals.q, kp, vp, scales, 0, b.req_to_token,
+                                              b.req_pool_indices, b.seq_lens, b.qo_indptr,
+                                              b.scale, causal=True)
+            else:
+                kp, vp = O.kv_store(vals.k_pool, vals.v_pool, 0, vals.k_new, vals.v_new, loc)
+                ref = O.prefill_attention(vals.q, kp, vp, 0, b.req_to_token,
+                                          b.req_pool_indices, b.seq_lens, b.qo_indptr, b.scale,
+                                          causal=True)
+            compare(A.out.float().cpu().numpy(), ref, "bf16", f"graph-replayed prefill ({kv})")
 
 
 def test_noalloc_decode_graph_replay():
