@@ -9,7 +9,9 @@ Covered:
   splits, ragged lengths and NaN codes in every slot no request maps;
 - the fused step (store, then attend), with its stored codes bit-exact;
 - packed prefill over FP8 pools, after the quantising store of the new
-  tokens, causal and not, for several group sizes and both head_dims;
+  tokens, causal and not, for several group sizes and both head_dims, and
+  with scores rising far past the first keys (tiles recomputed from their
+  exact row maxima);
 - cascade (shared-prefix) decode over FP8 pools;
 - the fused RoPE store: k codes (decided on the fp32 rotation) and v codes
   bit-exact, q within the rounding bound, untouched bytes and skipped
@@ -191,6 +193,52 @@ def test_prefill_fp8_parity(hq, hkv, d, causal):
                                   b.req_pool_indices, b.seq_lens, b.qo_indptr, b.scale,
                                   causal=causal)
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill g={hq // hkv} d={d} causal={causal}")
+
+
+def test_prefill_fp8_scores_rising_far_past_first_keys():
+    """E4M3 pools, q . k_j growing with j (scale 1, about 8 per key before
+    quantisation): later keys outscore the first 32 by far more than any fixed
+    headroom, so every tile that sees them is recomputed from its exact row
+    maxima, in the E4M3 instantiation too. K scale 1/4 keeps the codes below
+    the format's 448."""
+    b = W.custom("fp8_rising", n_layers=1, n_slots=4096, n_q_heads=8, n_kv_heads=2,
+                 head_dim=128, dtype="bf16", seq_lens=[300, 129, 40], n_new=[200, 129, 40],
+                 seed=660, scale=1.0)
+    scales = np.float32([[0.25, 2.0 ** -6]])
+    vals = W.host_values(b, 661)
+    q = np.zeros_like(vals.q)
+    q[:, :, 0] = 8.0
+    k_pool = vals.k_pool.copy()
+    k_new = vals.k_new.copy()
+    for i in range(b.batch):
+        L = int(b.seq_lens[i])
+        n = int(b.n_new[i])
+        P = L - n
+        row = b.req_to_token[b.req_pool_indices[i]]
+        for j in range(P):
+            k_pool[0, row[j], :, 0] = j / 8.0
+        lo = int(b.qo_indptr[i])
+        for t in range(n):
+            k_new[lo + t, :, 0] = (P + t) / 8.0
+    k_new = W.round_to_bf16(k_new)
+    kc = O.quantize(k_pool, scales[0, 0])
+    vc = O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens),
+                         to_dev(b.qo_indptr))
+    loc = torch.empty(b.total_q, dtype=torch.int32, device=DEV)
+    ops.build_metadata(meta, ops.PKV_MODE_PREFILL, None, None, loc, None)
+    ops.kv_store(kd, vd, 0, to_dev(k_new, torch.bfloat16), to_dev(vals.v_new, torch.bfloat16),
+                 loc, kv_scales=sd)
+    out = ops.paged_prefill_attn(to_dev(q, torch.bfloat16), kd, vd, 0, meta, b.max_q_len,
+                                 b.scale, True, kv_scales=sd)
+    torch.cuda.synchronize()
+    loc_h = O.prefill_locations(b.req_to_token, b.req_pool_indices, b.seq_lens, b.qo_indptr)
+    kc2, vc2 = O.kv_store_fp8(kc, vc, 0, k_new, vals.v_new, loc_h, scales)
+    assert np.array_equal(kd.cpu().numpy(), kc2) and np.array_equal(vd.cpu().numpy(), vc2)
+    ref = O.prefill_attention_fp8(q, kc2, vc2, scales, 0, b.req_to_token, b.req_pool_indices,
+                                  b.seq_lens, b.qo_indptr, b.scale, causal=True)
+    compare(out.float().cpu().numpy(), ref, "bf16", "fp8 prefill, rising scores")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
