@@ -195,14 +195,15 @@ def test_prefill_fp8_parity(hq, hkv, d, causal):
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill g={hq // hkv} d={d} causal={causal}")
 
 
-def test_prefill_fp8_scores_rising_far_past_first_keys():
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_fp8_scores_rising_far_past_first_keys(d):
     """E4M3 pools, q . k_j growing with j (scale 1, about 8 per key before
     quantisation): later keys outscore the first 32 by far more than any fixed
     headroom, so every tile that sees them is recomputed from its exact row
     maxima, in the E4M3 instantiation too. K scale 1/4 keeps the codes below
     the format's 448."""
     b = W.custom("fp8_rising", n_layers=1, n_slots=4096, n_q_heads=8, n_kv_heads=2,
-                 head_dim=128, dtype="bf16", seq_lens=[300, 129, 40], n_new=[200, 129, 40],
+                 head_dim=d, dtype="bf16", seq_lens=[300, 129, 40], n_new=[200, 129, 40],
                  seed=660, scale=1.0)
     scales = np.float32([[0.25, 2.0 ** -6]])
     vals = W.host_values(b, 661)
@@ -238,7 +239,7 @@ def test_prefill_fp8_scores_rising_far_past_first_keys():
     assert np.array_equal(kd.cpu().numpy(), kc2) and np.array_equal(vd.cpu().numpy(), vc2)
     ref = O.prefill_attention_fp8(q, kc2, vc2, scales, 0, b.req_to_token, b.req_pool_indices,
                                   b.seq_lens, b.qo_indptr, b.scale, causal=True)
-    compare(out.float().cpu().numpy(), ref, "bf16", "fp8 prefill, rising scores")
+    compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill, rising scores, head_dim {d}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
