@@ -3,8 +3,10 @@
 Covers the tiny fp32 workload (plain and NaN-poisoned), B=1 decode at 1K-32K,
 ragged batched decode with a shared prefix, and the large-batch stress
 workload (sampled requests); plus invariants (slot relocation, split count,
-L=1, equal keys), determinism, padded and recycled request rows, and the
-partials in the workspace against the oracle's split partials.
+L=1, equal keys), determinism, padded and recycled request rows, the
+partials in the workspace against the oracle's split partials, and scores
+rising along the sequence (the online softmax's stabiliser raised again and
+again, in both decode kernels).
 """
 
 import dataclasses
@@ -424,3 +426,30 @@ def test_decode_step_under_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
         _ = (db.q.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+@pytest.mark.parametrize("hq", [32, 64])
+def test_scores_rising_along_the_sequence(hq):
+    """q . k_j = j along each sequence (scale 1): every later tile outscores the
+    running stabiliser by more than its headroom, so the online softmax raises
+    it (and rescales what it holds) again and again; one request is a sawtooth
+    that falls back to low scores every 300 keys. g = 4 runs the VALU kernel,
+    g = 8 the MFMA one."""
+    lens = np.array([1500, 700, 33])
+    b = W.custom("decode_rising", n_layers=1, n_slots=4096, n_q_heads=hq, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens, n_new=np.ones(3, np.int64),
+                 seed=280, scale=1.0)
+    vals = W.host_values(b, 281)
+    q = np.zeros_like(vals.q)
+    q[:, :, 0] = 32.0
+    k_pool = vals.k_pool.copy()
+    for i in range(b.batch):
+        row = b.req_to_token[b.req_pool_indices[i]]
+        for j in range(int(b.seq_lens[i])):
+            k_pool[0, row[j], :, 0] = (j % 300 if i == 1 else j) / 32.0
+    vals = W.Values(q, vals.k_new, vals.v_new, W.round_to_bf16(k_pool), vals.v_pool)
+    db = DeviceBatch(b, vals)
+    out, _ = run_decode(db, 0, ops.split_cfg(8, 0, 256))
+    ref = O.decode_attention(q, vals.k_pool, vals.v_pool, 0, b.req_to_token, b.req_pool_indices,
+                             b.seq_lens, b.scale)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"rising decode scores, g={hq // 8}")

@@ -6,7 +6,8 @@ Covered:
   ties, a non-power-of-two scale, saturation beyond 448 and subnormal codes.
   Out-of-range locations are skipped and the other layer stays untouched;
 - decode parity for g = 1, 2, 4, 8, 16 and head_dim 64 / 128, with several
-  splits, ragged lengths and NaN codes in every slot no request maps;
+  splits, ragged lengths and NaN codes in every slot no request maps, and with
+  scores rising along the sequence (the stabiliser raised again and again);
 - the fused step (store, then attend), with its stored codes bit-exact;
 - packed prefill over FP8 pools, after the quantising store of the new
   tokens, causal and not, for several group sizes and both head_dims, and
@@ -240,6 +241,37 @@ def test_prefill_fp8_scores_rising_far_past_first_keys(d):
     ref = O.prefill_attention_fp8(q, kc2, vc2, scales, 0, b.req_to_token, b.req_pool_indices,
                                   b.seq_lens, b.qo_indptr, b.scale, causal=True)
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill, rising scores, head_dim {d}")
+
+
+def test_decode_fp8_scores_rising_along_the_sequence():
+    """E4M3 pools, q . k_j = j (scale 1; k codes up to 188 under a K scale of
+    1/4): the online softmax raises its stabiliser again and again; one request
+    is a sawtooth that falls back every 300 keys."""
+    lens = np.array([1500, 700, 33])
+    b = W.custom("fp8_decode_rising", n_layers=1, n_slots=4096, n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens, n_new=np.ones(3, np.int64),
+                 seed=680, scale=1.0)
+    scales = np.float32([[0.25, 2.0 ** -6]])
+    vals = W.host_values(b, 681)
+    q = np.zeros_like(vals.q)
+    q[:, :, 0] = 32.0
+    k_pool = vals.k_pool.copy()
+    for i in range(b.batch):
+        row = b.req_to_token[b.req_pool_indices[i]]
+        for j in range(int(b.seq_lens[i])):
+            k_pool[0, row[j], :, 0] = (j % 300 if i == 1 else j) / 32.0
+    kc = O.quantize(k_pool, scales[0, 0])
+    vc = O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens))
+    split = ops.split_cfg(8, 0, 256)
+    ws = ops.alloc_decode_workspace(b.batch, b.n_q_heads, b.head_dim, split.max_splits)
+    out = ops.paged_decode_attn(to_dev(q, torch.bfloat16), kd, vd, 0, meta, b.scale, split, ws,
+                                kv_scales=sd)
+    torch.cuda.synchronize()
+    ref = O.decode_attention_fp8(q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
+                                 b.seq_lens, b.scale)
+    compare(out.float().cpu().numpy(), ref, "bf16", "fp8 decode, rising scores")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
