@@ -7,8 +7,8 @@ groups with edge lengths (a suffix of one key, no suffix at all, a one-member
 group, a zero-length prefix) for g = 1, 2, 4, 8 and 16, head_dim 64,
 padded rows, determinism, agreement with the plain decode, and a check that
 only the first member's prefix table entries are read; groups of many members
-(ten column tiles) and a member with a different prefix length; capture into
-a HIP graph and replay.
+(ten column tiles) and a member with a different prefix length; scores rising
+along the sequence; capture into a HIP graph and replay.
 """
 
 import dataclasses
@@ -192,3 +192,26 @@ def test_cascade_graph_replay():
         if step == 0:
             compare(out_graph.float().cpu().numpy(), oracle(b, vals), "bf16",
                     "graph-replayed cascade")
+
+
+def test_cascade_scores_rising_along_the_sequence():
+    """q . k_j = j (scale 1) through a shared prefix and the private tails: the
+    online softmax raises its stabiliser again and again, in the prefix
+    workgroups and in the suffix splits."""
+    lens = [1500, 1200, 900, 40]
+    b = shared_batch("cascade_rising", lens, [[0, 1, 2]], [768], 580)
+    b = dataclasses.replace(b, scale=1.0)
+    vals = W.host_values(b, 581)
+    q = np.zeros_like(vals.q)
+    q[:, :, 0] = 32.0
+    k_pool = vals.k_pool.copy()
+    for i in range(b.batch):
+        row = b.req_to_token[b.req_pool_indices[i]]
+        for j in range(int(b.seq_lens[i])):
+            k_pool[0, row[j], :, 0] = j / 32.0
+    vals = W.Values(q, vals.k_new, vals.v_new, W.round_to_bf16(k_pool), vals.v_pool)
+    db = DeviceBatch(b, vals)
+    split = ops.split_cfg(8, 0, 256)
+    groups = groups_for(b, [[0, 1, 2]], [768])
+    out = run_cascade(db, groups, split)
+    compare(out.float().cpu().numpy(), oracle(b, vals), "bf16", "cascade, rising scores")
