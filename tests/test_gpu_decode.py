@@ -4,9 +4,9 @@ Covers the tiny fp32 workload (plain and NaN-poisoned), B=1 decode at 1K-32K,
 ragged batched decode with a shared prefix, and the large-batch stress
 workload (sampled requests); plus invariants (slot relocation, split count,
 L=1, equal keys), determinism, padded and recycled request rows, the
-partials in the workspace against the oracle's split partials, and scores
+partials in the workspace against the oracle's split partials, scores
 rising along the sequence (the online softmax's stabiliser raised again and
-again, in both decode kernels).
+again, in both decode kernels), and zero and negative softmax scales.
 """
 
 import dataclasses
@@ -453,3 +453,20 @@ def test_scores_rising_along_the_sequence(hq):
     ref = O.decode_attention(q, vals.k_pool, vals.v_pool, 0, b.req_to_token, b.req_pool_indices,
                              b.seq_lens, b.scale)
     compare(out.float().cpu().numpy(), ref, "bf16", f"rising decode scores, g={hq // 8}")
+
+
+@pytest.mark.parametrize("hq", [32, 64])
+@pytest.mark.parametrize("scale", [0.0, -0.0883883])
+def test_zero_and_negative_scale(hq, scale):
+    """A zero scale gives every visible key the same weight (the mean of V); a
+    negative one favours the lowest scores. Both decode kernels (g = 4, 8)."""
+    lens = np.array([900, 130, 1, 64])
+    b = W.custom("decode_scale", n_layers=1, n_slots=4096, n_q_heads=hq, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens, n_new=np.ones(4, np.int64),
+                 seed=290, scale=scale)
+    vals = W.host_values(b, 291)
+    db = DeviceBatch(b, vals)
+    out, _ = run_decode(db, 0, ops.split_cfg(8, 0, 256))
+    ref = O.decode_attention(vals.q, vals.k_pool, vals.v_pool, 0, b.req_to_token,
+                             b.req_pool_indices, b.seq_lens, b.scale)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"decode scale {scale}, g={hq // 8}")

@@ -6,8 +6,9 @@ Covered:
   ties, a non-power-of-two scale, saturation beyond 448 and subnormal codes.
   Out-of-range locations are skipped and the other layer stays untouched;
 - decode parity for g = 1, 2, 4, 8, 16 and head_dim 64 / 128, with several
-  splits, ragged lengths and NaN codes in every slot no request maps, and with
-  scores rising along the sequence (the stabiliser raised again and again);
+  splits, ragged lengths and NaN codes in every slot no request maps, with
+  scores rising along the sequence (the stabiliser raised again and again),
+  and with zero and negative softmax scales;
 - the fused step (store, then attend), with its stored codes bit-exact;
 - packed prefill over FP8 pools, after the quantising store of the new
   tokens, causal and not, for several group sizes and both head_dims, and
@@ -272,6 +273,30 @@ def test_decode_fp8_scores_rising_along_the_sequence():
     ref = O.decode_attention_fp8(q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
                                  b.seq_lens, b.scale)
     compare(out.float().cpu().numpy(), ref, "bf16", "fp8 decode, rising scores")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883])
+def test_decode_fp8_zero_and_negative_scale(scale):
+    """E4M3 pools with a zero softmax scale (the mean of the represented V
+    values) and a negative one (the K scale folds into it)."""
+    lens = np.array([900, 130, 1, 64])
+    b = W.custom("fp8_decode_scale", n_layers=1, n_slots=4096, n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens, n_new=np.ones(4, np.int64),
+                 seed=690, scale=scale)
+    scales = np.float32([[0.02, 2.0 ** -6]])
+    vals = W.host_values(b, 691)
+    kc = O.quantize(vals.k_pool, scales[0, 0])
+    vc = O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens))
+    split = ops.split_cfg(8, 0, 256)
+    ws = ops.alloc_decode_workspace(b.batch, b.n_q_heads, b.head_dim, split.max_splits)
+    out = ops.paged_decode_attn(to_dev(vals.q, torch.bfloat16), kd, vd, 0, meta, b.scale, split,
+                                ws, kv_scales=sd)
+    torch.cuda.synchronize()
+    ref = O.decode_attention_fp8(vals.q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
+                                 b.seq_lens, b.scale)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 decode, scale {scale}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
