@@ -11,9 +11,9 @@ Covered:
   and with zero and negative softmax scales;
 - the fused step (store, then attend), with its stored codes bit-exact;
 - packed prefill over FP8 pools, after the quantising store of the new
-  tokens, causal and not, for several group sizes and both head_dims, and
-  with scores rising far past the first keys (tiles recomputed from their
-  exact row maxima);
+  tokens, causal and not, for several group sizes and both head_dims, with
+  scores rising far past the first keys (tiles recomputed from their exact
+  row maxima), and with zero and negative softmax scales;
 - cascade (shared-prefix) decode over FP8 pools;
 - the fused RoPE store: k codes (decided on the fp32 rotation) and v codes
   bit-exact, q within the rounding bound, untouched bytes and skipped
@@ -297,6 +297,37 @@ def test_decode_fp8_zero_and_negative_scale(scale):
     ref = O.decode_attention_fp8(vals.q, kc, vc, scales, 0, b.req_to_token, b.req_pool_indices,
                                  b.seq_lens, b.scale)
     compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 decode, scale {scale}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883])
+def test_prefill_fp8_zero_and_negative_scale(scale):
+    """E4M3 prefill with a zero softmax scale (every visible key weighs the
+    same) and a negative one (applied as its magnitude on -Q, with the K scale
+    folded in)."""
+    lens = np.array([300, 70, 129])
+    n_new = np.array([64, 70, 33])
+    scales = np.float32([[0.02, 2.0 ** -6]])
+    b = W.custom("fp8_prefill_scale", n_layers=1, n_slots=4096, n_q_heads=32, n_kv_heads=8,
+                 head_dim=128, dtype="bf16", seq_lens=lens, n_new=n_new, seed=700, scale=scale)
+    vals = W.host_values(b, 701)
+    kc = O.quantize(vals.k_pool, scales[0, 0])
+    vc = O.quantize(vals.v_pool, scales[0, 1])
+    kd, vd, sd = to_dev(kc), to_dev(vc), to_dev(scales)
+    meta = ops.make_meta(to_dev(b.req_to_token), to_dev(b.req_pool_indices), to_dev(b.seq_lens),
+                         to_dev(b.qo_indptr))
+    loc = torch.empty(b.total_q, dtype=torch.int32, device=DEV)
+    ops.build_metadata(meta, ops.PKV_MODE_PREFILL, None, None, loc, None)
+    ops.kv_store(kd, vd, 0, to_dev(vals.k_new, torch.bfloat16), to_dev(vals.v_new, torch.bfloat16),
+                 loc, kv_scales=sd)
+    out = ops.paged_prefill_attn(to_dev(vals.q, torch.bfloat16), kd, vd, 0, meta, b.max_q_len,
+                                 b.scale, True, kv_scales=sd)
+    torch.cuda.synchronize()
+    loc_h = O.prefill_locations(b.req_to_token, b.req_pool_indices, b.seq_lens, b.qo_indptr)
+    kc2, vc2 = O.kv_store_fp8(kc, vc, 0, vals.k_new, vals.v_new, loc_h, scales)
+    ref = O.prefill_attention_fp8(vals.q, kc2, vc2, scales, 0, b.req_to_token,
+                                  b.req_pool_indices, b.seq_lens, b.qo_indptr, b.scale,
+                                  causal=True)
+    compare(out.float().cpu().numpy(), ref, "bf16", f"fp8 prefill, scale {scale}")
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (64, 8, 128), (16, 4, 64)])
