@@ -8,7 +8,8 @@ group, a zero-length prefix) for g = 1, 2, 4, 8 and 16, head_dim 64,
 padded rows, determinism, agreement with the plain decode, and a check that
 only the first member's prefix table entries are read; groups of many members
 (ten column tiles) and a member with a different prefix length; scores rising
-along the sequence; capture into a HIP graph and replay.
+along the sequence; zero and negative scales; capture into a HIP graph and
+replay.
 """
 
 import dataclasses
@@ -215,3 +216,17 @@ def test_cascade_scores_rising_along_the_sequence():
     groups = groups_for(b, [[0, 1, 2]], [768])
     out = run_cascade(db, groups, split)
     compare(out.float().cpu().numpy(), oracle(b, vals), "bf16", "cascade, rising scores")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883])
+def test_cascade_zero_and_negative_scale(scale):
+    """Zero and negative softmax scales through the shared prefix and the tails."""
+    lens = [900, 700, 1200, 300]
+    b = shared_batch("cascade_scale", lens, [[0, 1, 2]], [256], 590)
+    b = dataclasses.replace(b, scale=scale)
+    vals = W.host_values(b, 591)
+    db = DeviceBatch(b, vals)
+    split = ops.split_cfg(8, 0, 256)
+    groups = groups_for(b, [[0, 1, 2]], [256])
+    out = run_cascade(db, groups, split)
+    compare(out.float().cpu().numpy(), oracle(b, vals), "bf16", f"cascade, scale {scale}")
